@@ -1,0 +1,196 @@
+// C ABI of the library (declared in include/moe_fp4.h): argument checks,
+// workspace sizing and kernel launches on the caller's stream. No
+// allocation, no synchronisation, no device reads on the host.
+#include "../../include/moe_fp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int group_size(int fmt) { return fmt == MOE_FMT_NVFP4 ? 16 : (fmt == MOE_FMT_MXFP4 ? 32 : 0); }
+
+int check_desc(const moe_desc* d) {
+    if (!d) return fail(MOE_ERR_ARG, "desc is NULL");
+    const int G = group_size(d->format);
+    if (!G) return fail(MOE_ERR_ARG, "unknown format %d", d->format);
+    if (d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k <= 0)
+        return fail(MOE_ERR_ARG, "H, I, E, k must be positive (H=%d I=%d E=%d k=%d)", d->H, d->I, d->E, d->k);
+    if (d->k > d->E) return fail(MOE_ERR_ARG, "k=%d exceeds E=%d", d->k, d->E);
+    if (d->H % G || d->I % G) return fail(MOE_ERR_ARG, "H=%d and I=%d must be multiples of the group size %d", d->H, d->I, G);
+    return MOE_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+    if (!p) return fail(MOE_ERR_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(MOE_ERR_ARG, "%s is not %zu-byte aligned", name, align);
+    return MOE_OK;
+}
+
+int check_ws(const void* ws, size_t have, size_t need) {
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (have < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_block_bytes(const moe_desc* d) {
+    if (check_desc(d) != MOE_OK) return 0;
+    const size_t n = (size_t)3 * d->H * d->I;
+    return n / 2 + n / group_size(d->format);
+}
+
+int moe_block_layout(const moe_desc* d, int64_t off[7]) {
+    int r = check_desc(d);
+    if (r) return r;
+    if (!off) return fail(MOE_ERR_ARG, "off is NULL");
+    const int64_t codes = (int64_t)d->H * d->I / 2, scales = (int64_t)d->H * d->I / group_size(d->format);
+    off[0] = 0;
+    off[1] = codes;
+    off[2] = 2 * codes;
+    off[3] = 3 * codes;
+    off[4] = 3 * codes + scales;
+    off[5] = 3 * codes + 2 * scales;
+    off[6] = 3 * codes + 3 * scales;
+    return ok();
+}
+
+size_t moe_workspace_bytes(const moe_desc* d, int32_t T, int32_t mode) {
+    if (check_desc(d) != MOE_OK || T < 0) return 0;
+    switch (mode) {
+        case MOE_MODE_ROUTE: return moe::route_ws_bytes(T, d->E);
+        case MOE_MODE_DECODE: return moe::decode_ws_bytes(d->H, d->I, d->k);
+        case MOE_MODE_PREFILL: return moe::prefill_ws_bytes(d->format, d->H, d->I, d->E, d->k, T);
+        default: return 0;
+    }
+}
+
+int moe_route(const moe_desc* d, const float* x, int32_t T, const float* Wr, int32_t* idx, float* w,
+              float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+    int r;
+    if ((r = check_desc(d))) return r;
+    if (T < 1) return fail(MOE_ERR_ARG, "T=%d must be >= 1", T);
+    if ((r = check_ptr(x, 16, "x")) || (r = check_ptr(Wr, 16, "Wr")) || (r = check_ptr(idx, 4, "idx")) ||
+        (r = check_ptr(w, 4, "w")))
+        return r;
+    if (logits_out && !aligned(logits_out, 4)) return fail(MOE_ERR_ARG, "logits_out is not 4-byte aligned");
+    if (!moe::route_supported(d->H, d->E, d->k))
+        return fail(MOE_ERR_UNSUPPORTED, "router needs H %% 256 == 0, H <= 8192, E <= %d, k <= %d (H=%d E=%d k=%d)",
+                    moe::kMaxE, moe::kMaxK, d->H, d->E, d->k);
+    if ((r = check_ws(ws, ws_bytes, moe::route_ws_bytes(T, d->E)))) return r;
+    return hip_status(moe::launch_route(d->H, d->E, d->k, T, x, Wr, idx, w, logits_out, ws,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                      "router launch");
+}
+
+int moe_expert_decode(const moe_desc* d, const float* x, const void* const* expert_ptrs, const int32_t* idx,
+                      const float* w, const moe_shared* shared, float* y, void* ws, size_t ws_bytes, void* stream) {
+    int r;
+    if ((r = check_desc(d))) return r;
+    if ((r = check_ptr(x, 16, "x")) || (r = check_ptr(expert_ptrs, 8, "expert_ptrs")) ||
+        (r = check_ptr(idx, 4, "idx")) || (r = check_ptr(w, 4, "w")) || (r = check_ptr(y, 4, "y")))
+        return r;
+    if (shared) {
+        if ((r = check_ptr(shared->gate, 16, "shared->gate")) || (r = check_ptr(shared->up, 16, "shared->up")) ||
+            (r = check_ptr(shared->down, 16, "shared->down")))
+            return r;
+    }
+    if (d->k > moe::kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k=%d exceeds %d", d->k, moe::kMaxK);
+    moe::DecodePlan plan;
+    if (!moe::plan_decode(d->format, d->H, d->I, &plan))
+        return fail(MOE_ERR_UNSUPPORTED, "no decode kernel for H=%d I=%d (needs H %% 512 == 0, H <= 4096, I <= 4096)",
+                    d->H, d->I);
+    if ((r = check_ws(ws, ws_bytes, moe::decode_ws_bytes(d->H, d->I, d->k)))) return r;
+    return hip_status(moe::launch_decode(d->format, plan, d->E, d->H, d->I, d->k, x, expert_ptrs, idx, w,
+                                         shared ? shared->gate : nullptr, shared ? shared->up : nullptr,
+                                         shared ? shared->down : nullptr, y, ws,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                      "decode launch");
+}
+
+int moe_expert_prefill(const moe_desc* d, const float* x, int32_t T, const void* const* expert_ptrs,
+                       const int32_t* idx, const float* w, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                       const moe_prefill_debug* dbg, void* stream) {
+    int r;
+    if ((r = check_desc(d))) return r;
+    if (T < 1) return fail(MOE_ERR_ARG, "T=%d must be >= 1", T);
+    if ((r = check_ptr(x, 16, "x")) || (r = check_ptr(expert_ptrs, 8, "expert_ptrs")) ||
+        (r = check_ptr(idx, 4, "idx")) || (r = check_ptr(w, 4, "w")) || (r = check_ptr(out, 16, "out")))
+        return r;
+    if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return fail(MOE_ERR_ARG, "unknown out_dtype %d", out_dtype);
+    if (!moe::prefill_supported(d->format, d->H, d->I, d->E, d->k))
+        return fail(MOE_ERR_UNSUPPORTED, "no prefill kernel for format=%d H=%d I=%d E=%d k=%d", d->format, d->H, d->I,
+                    d->E, d->k);
+    if ((r = check_ws(ws, ws_bytes, moe::prefill_ws_bytes(d->format, d->H, d->I, d->E, d->k, T)))) return r;
+    moe::PrefillDebug pd = {};
+    if (dbg) {
+        pd.x_bf16 = dbg->x_bf16;
+        pd.x_codes = dbg->x_codes;
+        pd.x_scales = dbg->x_scales;
+        pd.h_pre = dbg->h_pre;
+        pd.h_q = dbg->h_q;
+        pd.perm = dbg->perm;
+        pd.off = dbg->off;
+    }
+    return hip_status(moe::launch_prefill(d->format, d->H, d->I, d->E, d->k, T, x, expert_ptrs, idx, w, out,
+                                          out_dtype == MOE_OUT_BF16, ws, dbg ? &pd : nullptr,
+                                          reinterpret_cast<hipStream_t>(stream)),
+                      "prefill launch");
+}
+
+int moe_dequant_block(const moe_desc* d, const void* block, float* gate, float* up, float* down, void* stream) {
+    int r;
+    if ((r = check_desc(d))) return r;
+    if ((r = check_ptr(block, 16, "block")) || (r = check_ptr(gate, 4, "gate")) || (r = check_ptr(up, 4, "up")) ||
+        (r = check_ptr(down, 4, "down")))
+        return r;
+    return hip_status(moe::launch_dequant(d->format, d->H, d->I, block, gate, up, down,
+                                          reinterpret_cast<hipStream_t>(stream)),
+                      "dequant launch");
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape (no tuned kernel)";
+        case MOE_ERR_HIP: return "HIP launch error";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

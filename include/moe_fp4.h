@@ -1,0 +1,202 @@
+/*
+ * moe_fp4.h - C ABI of the MI355X (gfx950) library for the routed
+ * mixture-of-experts FFN over block-scaled FP4 expert weights.
+ *
+ * The method (sources cited by title and section):
+ *  [Q] "Running a 133 GB MoE model on an 8 GB GPU at 11 tokens/s by streaming
+ *      experts from NVMe" (aiwithghost.com)
+ *  [D] "Running the 510 GB DeepSeek-V4.1-Flash on an 8 GB GPU, and three bugs
+ *      that never raise an error" (dev.to)
+ *
+ * One MoE layer: a router picks k of E experts per token from fp32 logits
+ * (softmax, top-k, weights renormalised over the chosen k; [Q] "Why this
+ * model, of all models": top-10 of 512; [D] "Bytes per token decide
+ * everything": 6 of 384). Each chosen expert is a SwiGLU FFN
+ * y = down(silu(gate x) * (up x)) whose three matrices are stored as 4-bit
+ * e2m1 codes with one scale per group of G codes ([Q] "The engine", item 4:
+ * NVFP4; [D] "Three bugs", item 2: ue8m0 scales). The layer output is the
+ * weighted sum of the chosen experts' outputs (plus an optional dense bf16
+ * shared expert). Decode runs one token; prefill runs the whole prompt
+ * through the layer at once with tokens grouped by expert ([Q] "The engine",
+ * item 5).
+ *
+ * Conventions for every entry point:
+ *  - All buffers are DEVICE memory owned by the caller unless stated. The
+ *    library never allocates, never synchronises, never reads device data on
+ *    the host and never copies to the host; every call only enqueues work on
+ *    `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code. Arguments are
+ *    validated on the host before anything is launched; on error nothing is
+ *    launched and moe_last_error() describes the problem (thread-local).
+ *  - A shape the library has no tuned kernel for returns
+ *    MOE_ERR_UNSUPPORTED; there is no slow or silent fallback.
+ *  - Faults inside kernels surface at the caller's next synchronisation.
+ *  - Workspace `ws`: device memory of at least moe_workspace_bytes() bytes,
+ *    256-byte aligned, ZERO-FILLED ONCE before its first use. Its first 4096
+ *    bytes hold completion counters that every call leaves at zero again.
+ *    Calls that share one workspace must not run concurrently.
+ *  - The library keeps no mutable global state and is reentrant.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Expert weight formats. Both use e2m1 codes (OCP MX FP4: magnitudes 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6 and a sign bit); they differ in the scale. */
+#define MOE_FMT_NVFP4 1 /* one E4M3 (OCP FP8 E4M3FN) scale per 16 codes */
+#define MOE_FMT_MXFP4 2 /* one UE8M0 (power-of-two) scale per 32 codes  */
+
+#define MOE_OK 0
+#define MOE_ERR_ARG (-1)         /* null / misaligned pointer, bad size or shape */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid, but no tuned kernel for this shape */
+#define MOE_ERR_HIP (-3)         /* a HIP launch failed */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace missing or too small */
+
+#define MOE_MODE_ROUTE 0
+#define MOE_MODE_DECODE 1
+#define MOE_MODE_PREFILL 2
+
+#define MOE_OUT_F32 0
+#define MOE_OUT_BF16 1
+
+/* Layer shape. H = hidden size, I = expert intermediate size, E = experts,
+ * k = experts per token, format = MOE_FMT_*. H and I must be multiples of
+ * the format's group size G (16 or 32). */
+typedef struct moe_desc {
+    int32_t H, I, E, k, format;
+} moe_desc;
+
+/* Dense bf16 shared expert (bit patterns, row-major): gate [I][H], up [I][H],
+ * down [H][I]. It is added to the layer output unweighted. */
+typedef struct moe_shared {
+    const uint16_t *gate;
+    const uint16_t *up;
+    const uint16_t *down;
+} moe_shared;
+
+/* Optional debug outputs of moe_expert_prefill (any member may be NULL).
+ * Rows in "grouped order" are indexed by position p in perm (rows of one
+ * expert are contiguous, see moe_expert_prefill). */
+typedef struct moe_prefill_debug {
+    uint16_t *x_bf16;   /* [T][H] x~ = bf16(x), NVFP4 layers */
+    uint8_t *x_codes;   /* [T][H/2] x~ e2m1 codes, MXFP4 layers (element 2i in the low nibble) */
+    uint8_t *x_scales;  /* [T][H/32] x~ UE8M0 scale bytes, MXFP4 layers */
+    float *h_pre;       /* [T*k][I] silu(g)*u before rounding, grouped order */
+    float *h_q;         /* [T*k][I] h~ (the rounded h, as fp32), grouped order */
+    int32_t *perm;      /* [T*k] assignment id t*k+j at each grouped position */
+    int32_t *off;       /* [E+1] first grouped position of each expert; off[E] = T*k */
+} moe_prefill_debug;
+
+/* ---------------------------------------------------------------------- */
+/* Expert block layout                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of one expert block: 3*H*I/2 code bytes + 3*H*I/G scale bytes.
+ * Region order gate | up | down | gate_scale | up_scale | down_scale, as the
+ * expert repack of [Q] "The engine", item 1 (2,764,800 B for the Qwen shape,
+ * H=2560, I=640, NVFP4; 18,800,640 B = 17.93 MiB for the DeepSeek shape,
+ * H=4096, I=2880, MXFP4, [D] "Bytes per token decide everything").
+ * gate/up are [I][H] and down is [H][I]; every matrix is row-major with the
+ * 4-bit codes packed along the row (element 2c in the low nibble of byte c of
+ * the row); scales are row-major [rows][cols/G] bytes. Returns 0 for an
+ * invalid descriptor. */
+size_t moe_block_bytes(const moe_desc *d);
+
+/* Byte offsets of the six regions (off[0..5]) and the block size (off[6]).
+ * Returns MOE_OK or MOE_ERR_ARG. Host memory. */
+int moe_block_layout(const moe_desc *d, int64_t off[7]);
+
+/* Workspace bytes needed by one call of the given mode for T tokens. */
+size_t moe_workspace_bytes(const moe_desc *d, int32_t T, int32_t mode);
+
+/* ---------------------------------------------------------------------- */
+/* Router                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/* For each token t < T: logits[t][e] = sum_h Wr[e][h] * x[t][h] (fp32
+ * accumulate); S = the k experts with the largest logits (ties: lower expert
+ * index first), written to idx[t][0..k) in that order; w[t][j] =
+ * softmax(logits[t])[S_j] / sum over S, i.e. the softmax weights
+ * renormalised over the chosen k ([Q] "Where the time actually goes": the
+ * router's chosen experts). Nothing is read back to the host.
+ *   x          [T][H] fp32, 16-B aligned
+ *   Wr         [E][H] fp32, 16-B aligned
+ *   idx        [T][k] int32 (out);  w [T][k] fp32 (out)
+ *   logits_out [T][E] fp32 (out) or NULL
+ * Requires H % 4 == 0, E <= 1024, k <= min(E, 32). */
+int moe_route(const moe_desc *d, const float *x, int32_t T, const float *Wr, int32_t *idx, float *w,
+              float *logits_out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Decode: one token                                                       */
+/* ---------------------------------------------------------------------- */
+
+/* y = sum_{j<k} w[j] * expert_{idx[j]}(x)  (+ shared(x) if shared != NULL)
+ * where expert_e(x) = down_e( silu(gate_e x) * (up_e x) ), silu(z) =
+ * z / (1 + exp(-z)), weights decoded on the fly from the block at
+ * expert_ptrs[e] (format per d->format), fp32 activations and fp32
+ * accumulation. The sum over j runs in increasing j, so results are
+ * bit-identical from run to run.
+ *   x           [H] fp32, 16-B aligned
+ *   expert_ptrs DEVICE array of E pointers (8-B aligned), each to one
+ *               256-B-aligned expert block (resident layers:
+ *               base + e * moe_block_bytes)
+ *   idx [k] int32, w [k] fp32: the routing (e.g. from moe_route)
+ *   shared      host struct of device pointers, or NULL
+ *   y           [H] fp32 (out)
+ * Requires H % 512 == 0, H <= 4096, I % 128 == 0 (NVFP4) or I % 32 == 0
+ * (MXFP4), I <= 4096, k <= 32. */
+int moe_expert_decode(const moe_desc *d, const float *x, const void *const *expert_ptrs, const int32_t *idx,
+                      const float *w, const moe_shared *shared, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Prefill: T tokens grouped by expert                                     */
+/* ---------------------------------------------------------------------- */
+
+/* out[t] = sum_{j<k} w[t][j] * down_e( Q( silu(gate_e x~_t) * (up_e x~_t) ) ),
+ * e = idx[t][j], for every token at once ([Q] "The engine", item 5: the
+ * whole prompt through each layer). Assignments a = t*k + j are grouped by
+ * expert with a stable counting sort (count, exclusive prefix scan, scatter;
+ * within an expert in increasing a) and each expert's rows are multiplied
+ * as one ragged GEMM. Activation rounding points:
+ *   NVFP4: x~ = bf16(x) and h~ = bf16(h) (round to nearest even); the
+ *          weights are dequantised to bf16 exactly; bf16 MFMA, fp32 accumulate.
+ *   MXFP4: x~ and h~ are converted to MXFP4 per 32 consecutive elements
+ *          (OCP MX: shared exponent floor(log2 max|v|) - 2, e2m1 codes by
+ *          round-to-nearest-even with saturation); scaled FP4 MFMA, fp32
+ *          accumulate.
+ * The combine runs in increasing j in fp32; out is fp32 [T][H] or, with
+ * out_dtype = MOE_OUT_BF16, bf16 [T][H] rounded from that fp32 sum.
+ *   x [T][H] fp32; idx, w [T][k]; expert_ptrs as for decode; dbg optional.
+ * Requires H % 128 == 0 and I % 64 == 0 (NVFP4) or H % 128 == 0 and
+ * I % 64 == 0 (MXFP4), k <= 32. */
+int moe_expert_prefill(const moe_desc *d, const float *x, int32_t T, const void *const *expert_ptrs,
+                       const int32_t *idx, const float *w, void *out, int32_t out_dtype, void *ws,
+                       size_t ws_bytes, const moe_prefill_debug *dbg, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Test support and errors                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* Dequantise one expert block to fp32 gate [I][H], up [I][H], down [H][I]
+ * (each weight is e2m1(code) * scale, exact in fp32). For bit-exact checks
+ * of the decode used by every kernel. */
+int moe_dequant_block(const moe_desc *d, const void *block, float *gate, float *up, float *down, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

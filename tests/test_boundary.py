@@ -1,0 +1,107 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, computes layouts and workspace sizes, and rejects bad arguments
+with documented status codes before launching anything (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_route_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "moe_fp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = header_symbols()
+    assert set(syms) == set(m.EXPORTS)
+    raw = C.CDLL(m.LIB_PATH)
+    for s in syms:
+        assert hasattr(raw, s), s
+
+
+def test_layout_matches_oracle(orc):
+    for fmt, H, I in (("nvfp4", 2560, 640), ("mxfp4", 4096, 2880), ("nvfp4", 512, 16), ("mxfp4", 1024, 96)):
+        d = m.desc(H, I, 8, 2, fmt)
+        assert m.moe_block_layout(d) == orc.layout(fmt, H, I)
+        assert m.moe_block_bytes(d) == orc.layout(fmt, H, I)[6]
+
+
+def test_workspace_sizes_positive_and_monotone():
+    d = m.desc(2560, 640, 512, 10, "nvfp4")
+    for mode in (m.MOE_MODE_ROUTE, m.MOE_MODE_DECODE):
+        assert m.moe_workspace_bytes(d, 1, mode) >= 4096
+    assert m.moe_workspace_bytes(d, 64, m.MOE_MODE_ROUTE) > m.moe_workspace_bytes(d, 1, m.MOE_MODE_ROUTE)
+    assert m.moe_workspace_bytes(m.desc(2560, 640, 512, 10, 7), 1, m.MOE_MODE_DECODE) == 0
+
+
+def _err(fn, *a):
+    with pytest.raises(m.MoeError) as ei:
+        fn(*a)
+    return ei.value.status
+
+
+FAKE = 1 << 20          # a 16-byte-aligned, never dereferenced address
+ODD = FAKE + 4          # misaligned for 16-byte arguments
+
+
+def test_descriptor_errors():
+    for bad in (m.desc(0, 640, 8, 2, "nvfp4"), m.desc(2560, 640, 8, 9, "nvfp4"),
+                m.desc(2560, 640 + 8, 8, 2, "nvfp4"), m.desc(2560, 640, 8, 2, 5)):
+        assert _err(m.moe_route, bad, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
+
+
+def test_route_argument_errors():
+    d = m.desc(2560, 640, 64, 10, "nvfp4")
+    assert _err(m.moe_route, d, None, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
+    assert _err(m.moe_route, d, ODD, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
+    assert _err(m.moe_route, d, FAKE, 0, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
+    assert _err(m.moe_route, d, FAKE, 1, FAKE, FAKE, FAKE, None, None, 0, 0) == m.MOE_ERR_WORKSPACE
+    assert _err(m.moe_route, d, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, 16, 0) == m.MOE_ERR_WORKSPACE
+    assert _err(m.moe_route, d, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE + 16, 1 << 20, 0) == m.MOE_ERR_WORKSPACE
+    big = m.desc(2560, 640, 2048, 10, "nvfp4")
+    assert _err(m.moe_route, big, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 24, 0) == m.MOE_ERR_UNSUPPORTED
+
+
+def test_decode_argument_errors():
+    d = m.desc(2560, 640, 64, 10, "nvfp4")
+    ok = dict(x=FAKE, ptrs=FAKE, idx=FAKE, w=FAKE, y=FAKE)
+    assert _err(m.moe_expert_decode, d, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
+    assert _err(m.moe_expert_decode, d, FAKE, FAKE + 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
+    assert _err(m.moe_expert_decode, d, FAKE, FAKE, FAKE, FAKE, (FAKE, None, FAKE), FAKE, FAKE, 1 << 20, 0) \
+        == m.MOE_ERR_ARG
+    assert _err(m.moe_expert_decode, d, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1024, 0) == m.MOE_ERR_WORKSPACE
+    odd_h = m.desc(2560 + 16, 640, 64, 10, "nvfp4")       # H not a multiple of 512
+    assert _err(m.moe_expert_decode, odd_h, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 24, 0) \
+        == m.MOE_ERR_UNSUPPORTED
+    big_k = m.desc(2560, 640, 64, 40, "nvfp4")
+    assert _err(m.moe_expert_decode, big_k, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 24, 0) \
+        == m.MOE_ERR_UNSUPPORTED
+    del ok
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert m.lib.moe_status_string(s)
+    assert m.lib.moe_status_string(-99) == b"unknown status"
+
+
+def test_oracle_and_library_share_nothing():
+    """The oracle and the GPU library import, include and link nothing of
+    each other."""
+    pkg = os.path.join(ROOT, "block_scaled_fp4_route_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.lower().replace("oracle-free", ""), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            txt = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "block_scaled_fp4_route_amd" not in txt and "moe_fp4.h" not in txt, f

@@ -1,0 +1,210 @@
+"""GPU parity of the decode path (router, FP4 GEMVs, combine) against the CPU
+oracle, through the C ABI. Inputs come from the seeded generator; the oracle
+gets host copies of the same inputs and never sees a GPU output.
+
+Bars: dequantised weights bit-exact; top-k indices bit-exact where the
+logits are exact (integer case) and otherwise equal up to oracle near-ties;
+outputs max|d|/max|ref| <= 1e-4 (fp32 activations, fp32 accumulation against
+fp64); reruns bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthgen as sg
+from gpu_helpers import NTHREADS, bf16_bits, cosine, host_blocks, layer_blocks, rel_err, same_f32_bits
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_scaled_fp4_route_amd as m
+    return m
+
+
+def _dequant_gpu(m, d, block):
+    H, I = d.H, d.I
+    g = torch.empty((I, H), dtype=torch.float32, device="cuda")
+    u = torch.empty((I, H), dtype=torch.float32, device="cuda")
+    dn = torch.empty((H, I), dtype=torch.float32, device="cuda")
+    m.moe_dequant_block(d, block, g, u, dn)
+    torch.cuda.synchronize()
+    return g.cpu().numpy(), u.cpu().numpy(), dn.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["qwen_layer_decode", "deepseek_decode"])
+def test_dequant_bitexact_full_shape(m, orc, name):
+    wl = sg.get(name)
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    blocks = layer_blocks(wl, 0, E=2)
+    for e in range(2):
+        got = _dequant_gpu(m, d, blocks[e])
+        ref = orc.dequant_block(wl.fmt, wl.H, wl.I, blocks[e].cpu().numpy())
+        for a, b in zip(got, ref):
+            assert same_f32_bits(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_dequant_bitexact_every_code_scale_pair(m, orc, fmt):
+    """Every group holds all 16 codes and the scale bytes cycle through all
+    256 values (NaN scales, subnormal and overflowing products included)."""
+    H = I = 256
+    G = 16 if fmt == "nvfp4" else 32
+    d = m.desc(H, I, 4, 1, fmt)
+    nb = 3 * H * I // 2
+    pattern = np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], np.uint8)
+    codes = np.tile(pattern, nb // 8)
+    scales = (np.arange(3 * H * I // G) % 256).astype(np.uint8)
+    blk = np.concatenate([codes, scales])
+    got = _dequant_gpu(m, d, torch.tensor(blk, device="cuda"))
+    ref = orc.dequant_block(fmt, H, I, blk)
+    for a, b in zip(got, ref):
+        assert same_f32_bits(a, b)
+
+
+def _decode_case(m, orc, wl, E, idx, w, x, blocks, shared=None):
+    d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    ptrs = m.expert_ptr_table(blocks)
+    y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    idx_d = torch.tensor(idx, dtype=torch.int32, device="cuda")
+    w_d = torch.tensor(w, dtype=torch.float32, device="cuda")
+    m.moe_expert_decode(d, x, ptrs, idx_d, w_d, shared, y, ws)
+    torch.cuda.synchronize()
+    hb = host_blocks(blocks, idx)
+    sh = None if shared is None else [bf16_bits(s) for s in shared]
+    ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x.cpu().numpy(), [hb[int(e)] for e in idx],
+                            np.asarray(w, np.float32).astype(np.float64), shared=sh, nthreads=NTHREADS)
+    return y.cpu().numpy(), ref, (d, ws, ptrs, idx_d, w_d, y)
+
+
+@pytest.mark.parametrize("name,E", [("qwen_layer_decode", 64), ("deepseek_decode", 24)])
+def test_decode_parity_given_routing(m, orc, name, E):
+    wl = sg.get(name)
+    blocks = layer_blocks(wl, 0, E=E)
+    for step in range(2):
+        x = sg.activations(wl, step, 0, T=1, device="cuda").view(-1)
+        idx, w = sg.decode_routing(sg.Workload(**{**wl.__dict__, "E": E}), 0, step)
+        got, ref, _ = _decode_case(m, orc, wl, E, idx.numpy(), w.numpy(), x, blocks)
+        err = rel_err(got, ref)
+        print(f"{name} step {step}: max|d|/max|ref| = {err:.3e} cosine {cosine(got, ref):.9f}")
+        assert err <= TOL
+
+
+def test_decode_parity_shared_expert_full_layer(m, orc):
+    """Qwen decode layer at full size: 512 resident experts, the bf16 shared
+    expert, routing by moe_route on the device (no host sync between)."""
+    wl = sg.get("qwen_decode")
+    blocks = layer_blocks(wl, 0)
+    Wr = sg.router_weights(wl, 0, device="cuda")
+    shared = [t.to("cuda") for t in sg.shared_expert(wl, 0, device="cuda")]
+    x = sg.activations(wl, 0, 0, T=1, device="cuda").view(-1)
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    wsr = m.alloc_workspace(d, 1, m.MOE_MODE_ROUTE)
+    wsd = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    idx = torch.empty(wl.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(wl.k, dtype=torch.float32, device="cuda")
+    y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    ptrs = m.expert_ptr_table(blocks)
+    m.moe_route(d, x, 1, Wr, idx, w, None, wsr)
+    m.moe_expert_decode(d, x, ptrs, idx, w, shared, y, wsd)
+    torch.cuda.synchronize()
+    lg, oidx, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
+    gi = idx.cpu().numpy()
+    assert (gi == oidx[0]).all(), (gi, oidx[0])
+    assert rel_err(w.cpu().numpy(), ow[0]) <= TOL
+    hb = host_blocks(blocks, gi)
+    ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x.cpu().numpy(), [hb[int(e)] for e in gi], ow[0],
+                            shared=[bf16_bits(s) for s in shared], nthreads=NTHREADS)
+    err = rel_err(y.cpu().numpy(), ref)
+    print(f"qwen full layer + shared: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL
+
+
+def test_decode_deterministic_reruns(m, orc):
+    wl = sg.get("qwen_layer_decode")
+    blocks = layer_blocks(wl, 0, E=16)
+    x = sg.activations(wl, 5, 0, T=1, device="cuda").view(-1)
+    idx, w = sg.decode_routing(sg.Workload(**{**wl.__dict__, "E": 16}), 0, 5)
+    _, _, (d, ws, ptrs, idx_d, w_d, y) = _decode_case(m, orc, wl, 16, idx.numpy(), w.numpy(), x, blocks)
+    first = y.clone()
+    for _ in range(5):
+        m.moe_expert_decode(d, x, ptrs, idx_d, w_d, None, y, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), first.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt,H,I,E,k", [
+    ("nvfp4", 512, 16, 3, 1),      # smallest shapes, one expert
+    ("nvfp4", 512, 48, 4, 4),      # k = E
+    ("mxfp4", 1024, 96, 5, 2),
+    ("nvfp4", 4096, 4096, 2, 2),   # largest supported H and I
+    ("mxfp4", 4096, 4096, 2, 1),
+    ("nvfp4", 3072, 1040, 6, 3),   # down rows of 130 dwords: ragged lane coverage
+])
+def test_decode_edge_shapes(m, orc, fmt, H, I, E, k):
+    wl = sg.Workload("edge", 90, H, I, E, k, fmt, 1, 1, False, "router", 0.0,
+                     0x18 if fmt == "nvfp4" else 121, 0x48 if fmt == "nvfp4" else 129, False)
+    blocks = layer_blocks(wl, 0)
+    x = sg.activations(wl, 0, 0, T=1, device="cuda").view(-1)
+    idx, w = sg.decode_routing(wl, 0, 0)
+    got, ref, _ = _decode_case(m, orc, wl, E, idx.numpy(), w.numpy(), x, blocks)
+    assert rel_err(got, ref) <= TOL
+
+
+# ------------------------------------------------------------------ router ---
+
+def _route_gpu(m, d, x, Wr, T, want_logits=True):
+    idx = torch.empty((T, d.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, d.k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, d.E), dtype=torch.float32, device="cuda") if want_logits else None
+    ws = m.alloc_workspace(d, T, m.MOE_MODE_ROUTE)
+    m.moe_route(d, x, T, Wr, idx, w, lg, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), (lg.cpu().numpy() if want_logits else None)
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 17, 40])
+@pytest.mark.parametrize("name", ["qwen_layer_decode", "qwen_decode", "deepseek_decode"])
+def test_route_parity(m, orc, name, T):
+    wl = sg.get(name)
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    Wr = sg.router_weights(wl, 0, device="cuda")
+    x = sg.activations(wl, 11, 0, T=T, device="cuda")
+    gi, gw, gl = _route_gpu(m, d, x, Wr, T)
+    ol, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
+    assert rel_err(gl, ol) <= TOL
+    for t in range(T):
+        if not (gi[t] == oi[t]).all():
+            # only a near-tie in the oracle's own logits may reorder the choice
+            diff = set(gi[t]) ^ set(oi[t])
+            vals = ol[t, list(diff)] if diff else ol[t, gi[t]]
+            assert np.ptp(vals) <= 1e-5 * np.abs(ol[t]).max(), (t, gi[t], oi[t])
+        else:
+            assert rel_err(gw[t], ow[t]) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 5, 33])
+def test_route_exact_logits_with_ties(m, orc, T):
+    """Small-integer router weights and activations make every logit exact in
+    fp32 in any summation order, and planted duplicates create ties, so the
+    GPU's chosen indices must equal the oracle's sort-based top-k bit for bit
+    (tie rule: lower expert index first)."""
+    H, E, k = 512, 64, 10
+    d = m.desc(H, 64, E, k, "nvfp4")
+    g = torch.Generator().manual_seed(123)
+    Wr = torch.randint(-3, 4, (E, H), generator=g).float()
+    Wr[7] = Wr[3]
+    Wr[40] = Wr[3]
+    Wr[12] = Wr[50]
+    x = torch.randint(-2, 3, (T, H), generator=g).float()
+    gi, gw, gl = _route_gpu(m, d, x.cuda(), Wr.cuda(), T)
+    ol, oi, ow = orc.route(x.numpy(), Wr.numpy(), k)
+    assert (gl == ol).all()
+    assert (gi == oi).all()
+    assert rel_err(gw, ow) <= TOL
