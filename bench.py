@@ -1,0 +1,249 @@
+"""Benchmark of the routed FP4 MoE FFN on one MI355X.
+
+Default workload: Qwen-shaped decode, 48 MoE layers x 512 NVFP4 experts
+(63.3 GiB resident in HBM) + one bf16 shared expert per layer, top-10, hidden
+2560, intermediate 640, one token per step with a fresh seeded activation
+vector per (step, layer). A step is one token through all 48 layers: per
+layer moe_route (router GEMV + softmax + top-k on the device) and
+moe_expert_decode (expert SwiGLU GEMVs + weighted combine + shared expert).
+The K timed steps are captured once as a HIP graph and replayed; inputs are
+resident in HBM before the timer starts.
+
+Prints ONE JSON line (see the "roofline" and "cpu_baseline" members).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefill)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def measure_copy_bandwidth(torch, nbytes=4 << 30, iters=10):
+    """Device-to-device copy of a 4 GiB buffer: bytes read + written per second."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / iters
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / s / 1e9
+
+
+class DecodeModel:
+    """All layers of a decode workload resident on the GPU."""
+
+    def __init__(self, m, sg, wl, replicas=1):
+        import torch
+        self.m, self.wl = m, wl
+        self.L = wl.layers * replicas
+        self.d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+        B = wl.block_bytes
+        t0 = time.time()
+        self.blocks = torch.empty((self.L * wl.E, B), dtype=torch.uint8, device="cuda")
+        for l in range(self.L):
+            sg.fill_layer_blocks(wl, l % wl.layers if replicas == 1 else l, self.blocks[l * wl.E:(l + 1) * wl.E])
+        self.Wr = torch.stack([sg.router_weights(wl, l, device="cuda") for l in range(self.L)])
+        self.shared = ([[t.contiguous() for t in sg.shared_expert(wl, l, device="cuda")] for l in range(self.L)]
+                       if wl.shared else [None] * self.L)
+        base = self.blocks.data_ptr()
+        self.ptrs = torch.tensor([[base + (l * wl.E + e) * B for e in range(wl.E)] for l in range(self.L)],
+                                 dtype=torch.int64, device="cuda")
+        self.ws_r = m.alloc_workspace(self.d, 1, m.MOE_MODE_ROUTE)
+        self.ws_d = m.alloc_workspace(self.d, 1, m.MOE_MODE_DECODE)
+        self.idx = torch.empty((self.L, wl.k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((self.L, wl.k), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((self.L, wl.H), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] resident: {self.blocks.numel() / 2**30:.2f} GiB experts in {self.L} layers, "
+            f"generated in {time.time() - t0:.1f} s")
+
+    def inputs(self, sg, steps):
+        import torch
+        wl = self.wl
+        return torch.stack([torch.stack([sg.activations(wl, s, l % wl.layers, T=1, device="cuda").view(-1)
+                                         for l in range(wl.layers)]) for s in range(steps)])
+
+    def layer(self, x, l, events=None):
+        m = self.m
+        if events is not None:
+            events[0].record()
+        m.moe_route(self.d, x, 1, self.Wr[l], self.idx[l], self.w[l], None, self.ws_r)
+        if events is not None:
+            events[1].record()
+        m.moe_expert_decode(self.d, x, self.ptrs[l], self.idx[l], self.w[l], self.shared[l], self.y[l], self.ws_d)
+        if events is not None:
+            events[2].record()
+
+    def step(self, xs, s, replica_offset=0):
+        for l in range(self.wl.layers):
+            self.layer(xs[s, l], replica_offset + l)
+
+
+def bytes_per_layer(wl):
+    experts = wl.k * wl.block_bytes
+    router = wl.E * wl.H * 4
+    shared = 3 * wl.H * wl.I * 2 if wl.shared else 0
+    act = wl.H * 4 * 2  # x in, y out (the router and the experts read the same x)
+    return experts, router, shared, act
+
+
+def cpu_baseline_decode(sg, wl, model, budget_s=20.0):
+    """The oracle on a bounded sample: the first layers of one token, with all
+    host cores, inputs copied to the host before the timer starts."""
+    import numpy as np
+    import torch
+    from oracle import oracle as O
+    O.build(force=False)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    nthreads = max(1, cores)
+    L = wl.layers
+    x = [sg.activations(wl, 0, l, T=1).numpy().reshape(-1) for l in range(L)]
+    Wr = [model.Wr[l].cpu().numpy() for l in range(L)]
+    sh = [None if s is None else [t.view(torch.int16).cpu().numpy().view(np.uint16) for t in s]
+          for s in model.shared[:L]]
+    done, t_total = 0, 0.0
+    while done < L and t_total < budget_s:
+        l = done
+        _, oi, ow = O.route(x[l], Wr[l], wl.k)
+        blks = [model.blocks[l * wl.E + int(e)].cpu().numpy() for e in oi[0]]
+        t0 = time.perf_counter()
+        O.route(x[l], Wr[l], wl.k)
+        O.moe_decode(wl.fmt, wl.H, wl.I, x[l], blks, ow[0], shared=sh[l], nthreads=nthreads)
+        t_total += time.perf_counter() - t0
+        done += 1
+    per_token = t_total / done * L
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"layers 0..{done - 1} of token 0 ({done} of {L} layers, each: fp64 router + "
+                      f"{wl.k} experts + shared), timed {t_total:.1f} s, extrapolated to {L} layers"}
+
+
+def run_decode(args, m, sg, torch):
+    wl = sg.get(args.workload)
+    replicas = args.replicas if args.replicas else (16 if wl.layers == 1 else 1)
+    model = DecodeModel(m, sg, wl, replicas=replicas)
+    K, W = args.steps, args.warmup
+    xs = model.inputs(sg, W + K)
+    nrep = replicas
+
+    def step(s):
+        model.step(xs, s, replica_offset=(s % nrep) * wl.layers if nrep > 1 else 0)
+
+    # eager warmup (also checks the calls)
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+
+    # per-call timing with HIP events on the launch stream (eager launches)
+    nprobe = min(3 * wl.layers, 48) if wl.layers > 1 else 32
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nprobe)]
+    for i in range(nprobe):
+        s = W + (i // wl.layers) % K
+        l = i % wl.layers
+        model.layer(xs[s % (W + K), l], (i % nrep) * wl.layers + l if nrep > 1 else l, events=evs[i])
+    torch.cuda.synchronize()
+    route_us = sum(e[0].elapsed_time(e[1]) for e in evs) / nprobe * 1e3
+    expert_us = sum(e[1].elapsed_time(e[2]) for e in evs) / nprobe * 1e3
+
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(W, W + K):
+            step(s)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        mode = "eager"
+    else:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for s in range(W, W + K):
+                    step(s)
+        torch.cuda.current_stream().wait_stream(cs)
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        mode = "hip_graph"
+
+    ms_per_step = elapsed / K * 1e3
+    tok_s = 1e3 / ms_per_step
+    experts, router, shared, act = bytes_per_layer(wl)
+    layer_bytes = experts + router + shared + act
+    step_bytes = layer_bytes * wl.layers
+    expert_call_bytes = experts + shared + act
+    achieved = expert_call_bytes / (expert_us * 1e-6) / 1e9
+    copy_gbps = measure_copy_bandwidth(torch)
+    res = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded SplitMix64; random-code FP4 experts, no trained weights)",
+        "config": {"workload": wl.name, "layers": wl.layers, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
+                   "intermediate": wl.I, "weights": wl.fmt, "shared_expert": "bf16" if wl.shared else None,
+                   "tokens_per_step": 1, "replicas": replicas, "launch": mode, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "moe_expert_decode (k_gateup + k_down)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": expert_call_bytes, "avg_us": round(expert_us, 3)},
+        "layer_us": round(ms_per_step * 1e3 / wl.layers, 3),
+        "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "route_us_eager": round(route_us, 3), "expert_us_eager": round(expert_us, 3),
+        "hbm_copy_GBps_measured": round(copy_gbps, 1),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(sg, wl, model)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen_decode")
+    ap.add_argument("--replicas", type=int, default=0, help="layer replicas to rotate through (cold timing)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_scaled_fp4_route_amd as m
+    import synthgen as sg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = sg.get(args.workload)
+    if wl.is_prefill:
+        raise SystemExit(f"workload {wl.name} is a prefill workload; not available in this bench yet")
+    res = run_decode(args, m, sg, torch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -2,11 +2,11 @@
 // layer ([Q] "The engine", item 4: a single-token SwiGLU expert kernel over
 // NVFP4 weights), re-designed for CDNA4:
 //  * k_gateup: gate and up rows of every chosen expert (plus the bf16 shared
-//    expert) against the LDS-staged activation vector, SiLU*mul epilogue.
-//  * k_down:   down rows of every chosen expert against its hidden vector;
-//    per-(expert, row block) partial sums, then the last workgroup of each row
-//    block (completion ticket) forms the weighted combine in fixed order.
-// Both are HBM-bound GEMVs: every code byte is read once with coalesced
+//    expert) against the LDS-staged activation vector, SiLU*mul epilogue;
+//  * k_down: down rows of every chosen expert against its hidden vector,
+//    unweighted partial rows per expert;
+//  * k_combine: the weighted sum of the partial rows in fixed expert order.
+// The GEMVs are HBM-bound: every code byte is read once with coalesced
 // dword loads (64 lanes x 4 B contiguous), e2m1 pairs are converted by
 // v_cvt_scalef32_pk_f32_fp4, the group scale is applied once per 8 codes in
 // registers, and rows are reduced with DPP.
@@ -41,56 +41,70 @@ bool plan_decode(int fmt, int H, int I, DecodePlan* p) {
     }
     if (p->down_D > 8 || H % p->down_RB) return false;
     p->down_nrb = H / p->down_RB;
-    if (p->down_nrb > kMaxCounters) return false;
+    if (p->down_nrb > kCntRoute - kCntDone) return false;
     return true;
 }
 
+struct DecodeArgs {
+    const float* x;
+    const void* const* expert_ptrs;
+    const int32_t* idx;
+    const float* w;
+    const uint16_t* sh_gate;
+    const uint16_t* sh_up;
+    const uint16_t* sh_down;
+    float* h;    // [(k+1)][I] SwiGLU hidden vectors
+    float* Yp;   // [(k+1)][H] unweighted down rows
+    float* y;    // [H]
+    int E, k, H, I;
+    int has_shared;
+    int gt_r;    // gate/up tiles per routed slot
+    int gt_s;    // gate/up tiles of the shared slot
+    int n_gate;  // gate/up workgroups
+    int nrb;     // down row blocks
+    int sh_sub;  // shared-expert down workgroups per row block
+};
+
 // ----------------------------------------------------------------------------
-// gate/up GEMV + SiLU*mul.
-// Grid: (k + shared) * wg_per_slot workgroups of 256 threads. Workgroup
-// (slot, tile): wave v handles row pairs pair0 .. pair0+P-1 with
-// pair0 = (tile*4 + v)*P; each pair is gate row i and up row i. Lane l reads
-// code dwords l + 64m (m < D) of every row: 8 codes at columns 8(l+64m)..+7,
-// whose 8 activations it keeps in registers. Gate codes [I][H/2] and up
-// codes [I][H/2] are adjacent in the block, as are their scales.
-template <int FMT, int D, int P>
-__global__ __launch_bounds__(256) void k_gateup(const float* __restrict__ x, const void* const* __restrict__ expert_ptrs,
-                                                const int32_t* __restrict__ idx, int E, int k, int I, int wg_per_slot,
-                                                const uint16_t* __restrict__ sh_gate, const uint16_t* __restrict__ sh_up,
-                                                float* __restrict__ h) {
+// gate/up rows + SiLU*mul for one tile.
+// Wave v handles row pairs pair0 .. pair0+P-1 (gate row i and up row i).
+// Lane l reads code dwords l + 64m (m < D) of every row: 8 codes at columns
+// 8(l+64m)..+7 whose activations it keeps in registers. Gate and up codes
+// ([I][H/2] each) are adjacent in the block, as are their scales; the bf16
+// shared expert uses the same lane/column map with 16-byte chunks.
+template <int FMT, int D, int P, bool SHARED>
+__device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, int pair0, f4v* xs) {
     constexpr int K = 512 * D;     // H
     constexpr int KD = K / 8;      // code dwords per row (= 16-byte bf16 chunks per shared row)
     constexpr int G = Fmt<FMT>::G;
     constexpr int KS = K / G;      // scale bytes per row
-    __shared__ f4v xs[K / 4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = blockIdx.x / wg_per_slot;
-    const int pair0 = ((blockIdx.x % wg_per_slot) * 4 + wave) * P;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int I = a.I;
+    const int np = min(P, I - pair0);  // wave-uniform; <= 0 for idle waves of the last tile
+    const int e = SHARED ? 0 : a.idx[slot];
+    // an expert index outside [0, E) poisons this slot instead of reading
+    // beyond the pointer table
+    const bool bad = !SHARED && (unsigned)e >= (unsigned)a.E;
 
-    for (int i = tid; i < K / 4; i += 256) xs[i] = reinterpret_cast<const f4v*>(x)[i];
-    __syncthreads();
-    float xr[8 * D];
+    // 1. weight loads first (they do not depend on x)
+    uint32_t wv[2 * P][D], sv[2 * P][D];
+    uint4 v[2 * P][D];
+    if (SHARED) {
+        const uint4* gq = reinterpret_cast<const uint4*>(a.sh_gate);
+        const uint4* uq = reinterpret_cast<const uint4*>(a.sh_up);
 #pragma unroll
-    for (int m = 0; m < D; m++) {
-        const f4v a = xs[2 * (lane + 64 * m)], b = xs[2 * (lane + 64 * m) + 1];
-        xr[8 * m + 0] = a.x; xr[8 * m + 1] = a.y; xr[8 * m + 2] = a.z; xr[8 * m + 3] = a.w;
-        xr[8 * m + 4] = b.x; xr[8 * m + 5] = b.y; xr[8 * m + 6] = b.z; xr[8 * m + 7] = b.w;
-    }
-    const int np = min(P, I - pair0);  // wave-uniform
-    if (np <= 0) return;
-
-    float acc[2 * P];
-    const int e = slot < k ? idx[slot] : 0;
-    if (slot < k && (unsigned)e >= (unsigned)E) {
-        // an expert index outside [0, E) poisons this slot's output instead of
-        // dereferencing a pointer beyond the table
+        for (int r = 0; r < 2 * P; r++) {
+            const int p = r % P;
+            const size_t row = (size_t)pair0 + p;
+            if (p < np) {
 #pragma unroll
-        for (int r = 0; r < 2 * P; r++) acc[r] = __uint_as_float(0x7FC00000u);
-    } else if (slot < k) {
-        const uint8_t* blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
+                for (int m = 0; m < D; m++) v[r][m] = (r < P ? gq : uq)[row * KD + lane + 64 * m];
+            }
+        }
+    } else if (!bad) {
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
         const uint32_t* codes = reinterpret_cast<const uint32_t*>(blk);
         const uint8_t* scl = blk + (size_t)3 * I * (K / 2);
-        uint32_t wv[2 * P][D], sv[2 * P][D];
 #pragma unroll
         for (int r = 0; r < 2 * P; r++) {
             const int p = r % P;
@@ -104,102 +118,86 @@ __global__ __launch_bounds__(256) void k_gateup(const float* __restrict__ x, con
                 }
             }
         }
+    }
+
+    // 2. x through LDS into registers: lane keeps columns 8(lane+64m)..+7
+    for (int i = tid; i < K / 4; i += 256) xs[i] = reinterpret_cast<const f4v*>(a.x)[i];
+    __syncthreads();
+    if (np > 0) {
+        float xr[8 * D];
 #pragma unroll
-        for (int r = 0; r < 2 * P; r++) {
-            float a = 0.f;
-            if (r % P < np) {
-#pragma unroll
-                for (int m = 0; m < D; m++) a = fmaf(scale_to_f32<FMT>(sv[r][m]), dot8_fp4(wv[r][m], &xr[8 * m]), a);
-            }
-            acc[r] = a;
+        for (int m = 0; m < D; m++) {
+            const f4v p0 = xs[2 * (lane + 64 * m)], p1 = xs[2 * (lane + 64 * m) + 1];
+            xr[8 * m + 0] = p0.x; xr[8 * m + 1] = p0.y; xr[8 * m + 2] = p0.z; xr[8 * m + 3] = p0.w;
+            xr[8 * m + 4] = p1.x; xr[8 * m + 5] = p1.y; xr[8 * m + 6] = p1.z; xr[8 * m + 7] = p1.w;
         }
-    } else {
-        // dense bf16 shared expert: 16-byte chunk c of a row holds columns 8c..8c+7
-        const uint4* gq = reinterpret_cast<const uint4*>(sh_gate);
-        const uint4* uq = reinterpret_cast<const uint4*>(sh_up);
-        uint4 v[2 * P][D];
+        // 3. dot products, row sums, SiLU*mul
+        float acc[2 * P];
 #pragma unroll
         for (int r = 0; r < 2 * P; r++) {
-            const int p = r % P;
-            const size_t row = (size_t)pair0 + p;
-            if (p < np) {
-#pragma unroll
-                for (int m = 0; m < D; m++) v[r][m] = (r < P ? gq : uq)[row * KD + lane + 64 * m];
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 2 * P; r++) {
-            float a = 0.f;
+            float s = 0.f;
             if (r % P < np) {
+                if (SHARED) {
 #pragma unroll
-                for (int m = 0; m < D; m++) {
-                    const float* xx = &xr[8 * m];
-                    a = fmaf(bf16_lo(v[r][m].x), xx[0], a); a = fmaf(bf16_hi(v[r][m].x), xx[1], a);
-                    a = fmaf(bf16_lo(v[r][m].y), xx[2], a); a = fmaf(bf16_hi(v[r][m].y), xx[3], a);
-                    a = fmaf(bf16_lo(v[r][m].z), xx[4], a); a = fmaf(bf16_hi(v[r][m].z), xx[5], a);
-                    a = fmaf(bf16_lo(v[r][m].w), xx[6], a); a = fmaf(bf16_hi(v[r][m].w), xx[7], a);
+                    for (int m = 0; m < D; m++) {
+                        const float* xx = &xr[8 * m];
+                        s = fmaf(bf16_lo(v[r][m].x), xx[0], s); s = fmaf(bf16_hi(v[r][m].x), xx[1], s);
+                        s = fmaf(bf16_lo(v[r][m].y), xx[2], s); s = fmaf(bf16_hi(v[r][m].y), xx[3], s);
+                        s = fmaf(bf16_lo(v[r][m].z), xx[4], s); s = fmaf(bf16_hi(v[r][m].z), xx[5], s);
+                        s = fmaf(bf16_lo(v[r][m].w), xx[6], s); s = fmaf(bf16_hi(v[r][m].w), xx[7], s);
+                    }
+                } else if (!bad) {
+#pragma unroll
+                    for (int m = 0; m < D; m++)
+                        s = fmaf(scale_to_f32<FMT>(sv[r][m]), dot8_fp4(wv[r][m], &xr[8 * m]), s);
+                } else {
+                    s = __uint_as_float(0x7FC00000u);
                 }
             }
-            acc[r] = a;
+            acc[r] = wave_sum(s);
         }
-    }
+        if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < 2 * P; r++) acc[r] = wave_sum(acc[r]);
-    if (lane == 0) {
-#pragma unroll
-        for (int p = 0; p < P; p++)
-            if (p < np) h[(size_t)slot * I + pair0 + p] = silu_mul(acc[p], acc[P + p]);
+            for (int p = 0; p < P; p++)
+                if (p < np) a.h[(size_t)slot * I + pair0 + p] = silu_mul(acc[p], acc[P + p]);
+        }
     }
 }
 
 // ----------------------------------------------------------------------------
-// down GEMV + weighted combine.
-// Grid: nslots * nrb workgroups of 256 threads; workgroup (slot, rb) computes
-// rows rb*RB .. +RB of slot's down matrix against h[slot] (staged in LDS).
+// down rows of one slot for one row block, then (last arrival) the combine.
 // A row is covered by L lanes (64/L rows per wave pass); lane s of a row
-// reads code dwords s + L*m (m < D, while < I/8). Partial rows go to
-// Yp[slot][row]; the workgroup that completes row block rb last (ticket
-// cnt[rb]) writes y[row] = sum_j w[j] * Yp[j][row] (+ Yp[k][row]) in
-// increasing j, and resets cnt[rb] to zero.
-template <int FMT, int L, int D, int PASSES>
-__global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const void* const* __restrict__ expert_ptrs,
-                                              const int32_t* __restrict__ idx, const float* __restrict__ w, int E,
-                                              int k, int nslots, int H, int I, const uint16_t* __restrict__ sh_down,
-                                              float* __restrict__ Yp, int* __restrict__ cnt, float* __restrict__ y) {
+// reads code dwords s + L*m (m < D, while < I/8) and keeps the matching 8D
+// hidden values in registers. The weight loads are issued before waiting
+// for the slot's hidden vector, so they overlap the gate/up phase.
+template <int FMT, int L, int D, int PASSES, bool SHARED>
+__device__ __forceinline__ void down_tile(const DecodeArgs& a, int slot, int row_base, f4v* hs) {
     constexpr int G = Fmt<FMT>::G;
-    constexpr int RPW = 64 / L;                // rows per wave pass
-    constexpr int RB = 4 * RPW * PASSES;       // rows per workgroup
-    __shared__ f4v hs[kMaxI / 4];
-    __shared__ int is_last;
+    constexpr int RPW = 64 / L;  // rows per wave pass
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nrb = H / RB;
-    const int slot = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+    const int H = a.H, I = a.I;
     const int KD = I / 8, KS = I / G;
-
-    for (int i = tid; i < I / 4; i += 256) hs[i] = reinterpret_cast<const f4v*>(h + (size_t)slot * I)[i];
-    __syncthreads();
     const int grp = lane / L, s = lane % L;
-    float hr[8 * D];
-#pragma unroll
-    for (int m = 0; m < D; m++) {
-        const int c = s + L * m;
-        f4v a = {0.f, 0.f, 0.f, 0.f}, b = a;
-        if (c < KD) { a = hs[2 * c]; b = hs[2 * c + 1]; }
-        hr[8 * m + 0] = a.x; hr[8 * m + 1] = a.y; hr[8 * m + 2] = a.z; hr[8 * m + 3] = a.w;
-        hr[8 * m + 4] = b.x; hr[8 * m + 5] = b.y; hr[8 * m + 6] = b.z; hr[8 * m + 7] = b.w;
-    }
-    const int row0 = rb * RB + wave * (RPW * PASSES) + grp;  // row of pass q: row0 + q * RPW
+    const int row0 = row_base + wave * (RPW * PASSES) + grp;  // row of pass q: row0 + q * RPW
+    const int e = SHARED ? 0 : a.idx[slot];
+    const bool bad = !SHARED && (unsigned)e >= (unsigned)a.E;
 
-    float part[PASSES];
-    const int e = slot < k ? idx[slot] : 0;
-    if (slot < k && (unsigned)e >= (unsigned)E) {
+    // 1. weight loads
+    uint32_t wv[PASSES][D], sv[PASSES][D];
+    uint4 v[PASSES][D];
+    if (SHARED) {
+        const uint4* dq = reinterpret_cast<const uint4*>(a.sh_down);
 #pragma unroll
-        for (int q = 0; q < PASSES; q++) part[q] = __uint_as_float(0x7FC00000u);
-    } else if (slot < k) {
-        const uint8_t* blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
+        for (int q = 0; q < PASSES; q++) {
+            const size_t row = (size_t)row0 + q * RPW;
+#pragma unroll
+            for (int m = 0; m < D; m++)
+                if (s + L * m < KD) v[q][m] = dq[row * KD + s + L * m];
+        }
+    } else if (!bad) {
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
         const uint32_t* codes = reinterpret_cast<const uint32_t*>(blk + (size_t)I * H);  // after gate, up
         const uint8_t* scl = blk + (size_t)3 * I * H / 2 + (size_t)2 * I * H / G;
-        uint32_t wv[PASSES][D], sv[PASSES][D];
 #pragma unroll
         for (int q = 0; q < PASSES; q++) {
             const size_t row = (size_t)row0 + q * RPW;
@@ -212,87 +210,103 @@ __global__ __launch_bounds__(256) void k_down(const float* __restrict__ h, const
                 }
             }
         }
+    }
+
+    // 2. the slot's hidden vector through LDS into registers
+    for (int i = tid; i < I / 4; i += 256) hs[i] = reinterpret_cast<const f4v*>(a.h + (size_t)slot * I)[i];
+    __syncthreads();
+    float hr[8 * D];
 #pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            float a = 0.f;
+    for (int m = 0; m < D; m++) {
+        const int c = s + L * m;
+        f4v p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+        if (c < KD) { p0 = hs[2 * c]; p1 = hs[2 * c + 1]; }
+        hr[8 * m + 0] = p0.x; hr[8 * m + 1] = p0.y; hr[8 * m + 2] = p0.z; hr[8 * m + 3] = p0.w;
+        hr[8 * m + 4] = p1.x; hr[8 * m + 5] = p1.y; hr[8 * m + 6] = p1.z; hr[8 * m + 7] = p1.w;
+    }
+
+    // 3. dot products and row sums
 #pragma unroll
-            for (int m = 0; m < D; m++)
-                if (s + L * m < KD) a = fmaf(scale_to_f32<FMT>(sv[q][m]), dot8_fp4(wv[q][m], &hr[8 * m]), a);
-            part[q] = a;
-        }
-    } else {
-        const uint4* dq = reinterpret_cast<const uint4*>(sh_down);
-        uint4 v[PASSES][D];
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            const size_t row = (size_t)row0 + q * RPW;
-#pragma unroll
-            for (int m = 0; m < D; m++)
-                if (s + L * m < KD) v[q][m] = dq[row * KD + s + L * m];
-        }
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            float a = 0.f;
+    for (int q = 0; q < PASSES; q++) {
+        float acc = 0.f;
+        if (SHARED) {
 #pragma unroll
             for (int m = 0; m < D; m++) {
                 if (s + L * m < KD) {
                     const float* xx = &hr[8 * m];
-                    a = fmaf(bf16_lo(v[q][m].x), xx[0], a); a = fmaf(bf16_hi(v[q][m].x), xx[1], a);
-                    a = fmaf(bf16_lo(v[q][m].y), xx[2], a); a = fmaf(bf16_hi(v[q][m].y), xx[3], a);
-                    a = fmaf(bf16_lo(v[q][m].z), xx[4], a); a = fmaf(bf16_hi(v[q][m].z), xx[5], a);
-                    a = fmaf(bf16_lo(v[q][m].w), xx[6], a); a = fmaf(bf16_hi(v[q][m].w), xx[7], a);
+                    acc = fmaf(bf16_lo(v[q][m].x), xx[0], acc); acc = fmaf(bf16_hi(v[q][m].x), xx[1], acc);
+                    acc = fmaf(bf16_lo(v[q][m].y), xx[2], acc); acc = fmaf(bf16_hi(v[q][m].y), xx[3], acc);
+                    acc = fmaf(bf16_lo(v[q][m].z), xx[4], acc); acc = fmaf(bf16_hi(v[q][m].z), xx[5], acc);
+                    acc = fmaf(bf16_lo(v[q][m].w), xx[6], acc); acc = fmaf(bf16_hi(v[q][m].w), xx[7], acc);
                 }
             }
-            part[q] = a;
-        }
-    }
+        } else if (!bad) {
 #pragma unroll
-    for (int q = 0; q < PASSES; q++) {
-        const float r = (L == 16) ? row16_sum(part[q]) : wave_sum(part[q]);
-        if (s == 0) Yp[(size_t)slot * H + row0 + q * RPW] = r;
-    }
-
-    // completion ticket for row block rb
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(&cnt[rb], 1) == nslots - 1;
-    __syncthreads();
-    if (is_last) {
-        __threadfence();
-        for (int r = tid; r < RB; r += 256) {
-            const int row = rb * RB + r;
-            float acc = 0.f;
-            for (int j = 0; j < k; j++) acc = fmaf(w[j], Yp[(size_t)j * H + row], acc);
-            if (nslots > k) acc += Yp[(size_t)k * H + row];
-            y[row] = acc;
+            for (int m = 0; m < D; m++)
+                if (s + L * m < KD) acc = fmaf(scale_to_f32<FMT>(sv[q][m]), dot8_fp4(wv[q][m], &hr[8 * m]), acc);
         }
-        if (tid == 0) cnt[rb] = 0;
+        if (bad) acc = __uint_as_float(0x7FC00000u);
+        const float r = (L == 16) ? row16_sum(acc) : wave_sum(acc);
+        if (s == 0) a.Yp[(size_t)slot * H + row0 + q * RPW] = r;
     }
 }
 
 // ----------------------------------------------------------------------------
+// Three launches per call; the kernel boundaries carry the gate/up -> down ->
+// combine dependencies (cheaper on this chip than in-kernel device-scope
+// hand-offs between workgroups).
+template <int FMT, int GD, int GP>
+__global__ __launch_bounds__(256) void k_gateup(DecodeArgs a) {
+    __shared__ f4v buf[1024];  // x, H <= 4096
+    const int bid = blockIdx.x;
+    const int ng_r = a.k * a.gt_r;
+    if (bid < ng_r) {
+        const int slot = bid / a.gt_r, tile = bid % a.gt_r;
+        gateup_tile<FMT, GD, GP, false>(a, slot, (tile * 4 + (threadIdx.x >> 6)) * GP, buf);
+    } else {
+        // shared expert: bf16 rows are 3.5x the bytes of an FP4 row, one pair per wave
+        gateup_tile<FMT, GD, 1, true>(a, a.k, (bid - ng_r) * 4 + (threadIdx.x >> 6), buf);
+    }
+}
+
+template <int FMT, int DL, int DD, int DP>
+__global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
+    __shared__ f4v buf[1024];  // h, I <= 4096
+    constexpr int RPW = 64 / DL;
+    constexpr int RB = 4 * RPW * DP;  // rows per routed down workgroup
+    const int d = blockIdx.x;
+    if (d < a.k * a.nrb) {
+        down_tile<FMT, DL, DD, DP, false>(a, d / a.nrb, (d % a.nrb) * RB, buf);
+    } else {
+        // shared expert: its row blocks are split into sh_sub workgroups of one pass
+        down_tile<FMT, DL, DD, 1, true>(a, a.k, (d - a.k * a.nrb) * (4 * RPW), buf);
+    }
+}
+
+// y[row] = sum_{j<k} w[j] * Yp[j][row] (+ Yp[k][row] for the shared expert),
+// in increasing j.
+__global__ __launch_bounds__(256) void k_combine(DecodeArgs a) {
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= a.H) return;
+    float acc = 0.f;
+    for (int j = 0; j < a.k; j++) acc = fmaf(a.w[j], a.Yp[(size_t)j * a.H + row], acc);
+    if (a.has_shared) acc += a.Yp[(size_t)a.k * a.H + row];
+    a.y[row] = acc;
+}
+
 template <int FMT>
-static hipError_t launch_gateup(const DecodePlan& p, int E, int I, int nslots, int k, const float* x,
-                                const void* const* ep, const int32_t* idx, const uint16_t* sg, const uint16_t* su,
-                                float* h, hipStream_t s) {
-    dim3 grid(nslots * p.gate_wg_per_slot), block(256);
-#define GU(DD, PP) \
-    case DD: hipLaunchKernelGGL((k_gateup<FMT, DD, PP>), grid, block, 0, s, x, ep, idx, E, k, I, p.gate_wg_per_slot, sg, su, h); break;
+static hipError_t launch_expert(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
+    const int n_down = a.k * a.nrb + (a.has_shared ? a.nrb * a.sh_sub : 0);
+    dim3 block(256);
+#define GU(GD, GP) case GD: hipLaunchKernelGGL((k_gateup<FMT, GD, GP>), dim3(a.n_gate), block, 0, s, a); break;
     switch (p.gate_D) {
         GU(1, 4) GU(2, 4) GU(3, 4) GU(4, 4) GU(5, 4) GU(6, 2) GU(7, 2) GU(8, 2)
         default: return hipErrorInvalidValue;
     }
 #undef GU
-    return hipGetLastError();
-}
-
-template <int FMT>
-static hipError_t launch_down(const DecodePlan& p, int E, int H, int I, int nslots, int k, const float* h,
-                              const void* const* ep, const int32_t* idx, const float* w, const uint16_t* sd,
-                              float* Yp, int* cnt, float* y, hipStream_t s) {
-    dim3 grid(nslots * p.down_nrb), block(256);
-#define DN(LL, DD, PS) \
-    case DD: hipLaunchKernelGGL((k_down<FMT, LL, DD, PS>), grid, block, 0, s, h, ep, idx, w, E, k, nslots, H, I, sd, Yp, cnt, y); break;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define DN(DL, DD, DP) case DD: hipLaunchKernelGGL((k_down<FMT, DL, DD, DP>), dim3(n_down), block, 0, s, a); break;
     if (p.down_L == 16) {
         switch (p.down_D) {
             DN(16, 1, 4) DN(16, 2, 4) DN(16, 3, 4) DN(16, 4, 4) DN(16, 5, 4) DN(16, 6, 4) DN(16, 7, 4) DN(16, 8, 4)
@@ -305,6 +319,9 @@ static hipError_t launch_down(const DecodePlan& p, int E, int H, int I, int nslo
         }
     }
 #undef DN
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_combine, dim3((a.H + 255) / 256), block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -312,20 +329,21 @@ hipError_t launch_decode(int fmt, const DecodePlan& p, int E, int H, int I, int 
                          const void* const* expert_ptrs, const int32_t* idx, const float* w,
                          const uint16_t* sh_gate, const uint16_t* sh_up, const uint16_t* sh_down, float* y,
                          void* ws, hipStream_t s) {
-    const int nslots = k + (sh_gate ? 1 : 0);
     char* base = reinterpret_cast<char*>(ws);
-    int* cnt = reinterpret_cast<int*>(base);
-    float* hbuf = reinterpret_cast<float*>(base + kCounterBytes);
-    float* Yp = reinterpret_cast<float*>(base + kCounterBytes + align256((size_t)(k + 1) * I * sizeof(float)));
-    hipError_t e;
-    if (fmt == kFmtNvfp4) {
-        e = launch_gateup<kFmtNvfp4>(p, E, I, nslots, k, x, expert_ptrs, idx, sh_gate, sh_up, hbuf, s);
-        if (e != hipSuccess) return e;
-        return launch_down<kFmtNvfp4>(p, E, H, I, nslots, k, hbuf, expert_ptrs, idx, w, sh_down, Yp, cnt, y, s);
-    }
-    e = launch_gateup<kFmtMxfp4>(p, E, I, nslots, k, x, expert_ptrs, idx, sh_gate, sh_up, hbuf, s);
-    if (e != hipSuccess) return e;
-    return launch_down<kFmtMxfp4>(p, E, H, I, nslots, k, hbuf, expert_ptrs, idx, w, sh_down, Yp, cnt, y, s);
+    DecodeArgs a;
+    a.x = x; a.expert_ptrs = expert_ptrs; a.idx = idx; a.w = w;
+    a.sh_gate = sh_gate; a.sh_up = sh_up; a.sh_down = sh_down;
+    a.h = reinterpret_cast<float*>(base + kCounterBytes);
+    a.Yp = reinterpret_cast<float*>(base + kCounterBytes + align256((size_t)(k + 1) * I * sizeof(float)));
+    a.y = y;
+    a.E = E; a.k = k; a.H = H; a.I = I;
+    a.has_shared = sh_gate ? 1 : 0;
+    a.gt_r = p.gate_wg_per_slot;
+    a.gt_s = (I + 3) / 4;  // shared gate/up: one row pair per wave
+    a.n_gate = k * a.gt_r + (a.has_shared ? a.gt_s : 0);
+    a.nrb = p.down_nrb;
+    a.sh_sub = p.down_RB / (4 * (64 / p.down_L));
+    return fmt == kFmtNvfp4 ? launch_expert<kFmtNvfp4>(p, a, s) : launch_expert<kFmtMxfp4>(p, a, s);
 }
 
 // ----------------------------------------------------------------------------

@@ -2,9 +2,9 @@
 // weights renormalised over the chosen k, computed on the device so the
 // chosen experts never travel to the host (the pages' engine read them back
 // once per layer, [Q] "Where the time actually goes").
-//  * k_route_split (T <= 16): one wave per (expert row, token) so the E x H
-//    fp32 router matrix streams from HBM over the whole chip; the wave that
-//    finishes a token last (ticket) runs the top-k for it.
+//  * k_route_logits + k_route_topk (T <= 16): one wave per (expert row,
+//    token) so the E x H fp32 router matrix streams from HBM over the whole
+//    chip, then one wave per token runs the top-k.
 //  * k_route_tokens (T > 16): one workgroup per token computes all E logits
 //    into LDS and runs the top-k itself.
 #include "moe_device.h"
@@ -16,47 +16,45 @@ size_t route_ws_bytes(int T, int E) { return kCounterBytes + align256((size_t)T 
 
 bool route_supported(int H, int E, int k) { return H % 256 == 0 && H <= 8192 && E >= 1 && E <= kMaxE && k >= 1 && k <= kMaxK && k <= E; }
 
-// Order key: larger logit first, lower expert index first among equal
-// logits. -0 is folded onto +0 so that equal values tie.
-__device__ __forceinline__ unsigned long long rank_key(float v, int e) {
-    uint32_t u = __float_as_uint(v + 0.0f);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)u << 32) | (0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-// Top-k of l[0..E) (E <= 1024) by one full wave; writes idx[0..k) and the
-// renormalised softmax weights w[0..k).
-__device__ void topk_wave(const float* l, int E, int k, int32_t* idx, float* w) {
+// Top-k of E <= 1024 logits by one full wave; writes idx[0..k) (larger logit
+// first, lower expert index first among equal logits) and the softmax
+// weights renormalised over the chosen k. LOAD(e) reads logit e. Each round
+// takes the wave maximum with DPP, then the lowest expert index holding it
+// via a ballot.
+template <class LOAD>
+__device__ void topk_wave(LOAD load, int E, int k, int32_t* idx, float* w) {
+    constexpr int NI = kMaxE / 64;
     const int lane = threadIdx.x & 63;
-    unsigned long long key[kMaxE / 64];
+    const float NEG = -__builtin_inff();
+    float v[NI];
 #pragma unroll
-    for (int i = 0; i < kMaxE / 64; i++) {
+    for (int i = 0; i < NI; i++) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? rank_key(l[e], e) : 0ull;
+        v[i] = e < E ? load(e) + 0.0f : NEG;  // + 0 folds -0 onto +0
     }
-    int my_e = 0;  // lane j < k keeps the j-th chosen expert
+    int my_e = 0;
+    float my_l = 0.f;
     for (int j = 0; j < k; j++) {
-        unsigned long long best = 0ull;
+        float m = v[0];
 #pragma unroll
-        for (int i = 0; i < kMaxE / 64; i++) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+        for (int i = 1; i < NI; i++) m = fmaxf(m, v[i]);
+        m = wave_max(m);
+        int e = -1;  // wave-uniform
 #pragma unroll
-        for (int i = 0; i < kMaxE / 64; i++)
-            if (lane + 64 * i == e) key[i] = 0ull;
-        if (lane == j) my_e = e;
+        for (int i = 0; i < NI; i++) {
+            const unsigned long long mask = __ballot(v[i] == m);
+            if (e < 0 && mask) e = (__ffsll((long long)mask) - 1) + 64 * i;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+            if (lane + 64 * i == e) v[i] = NEG;
+        if (lane == j) {
+            my_e = e;
+            my_l = m;
+        }
     }
-    const float lmax = l[__shfl(my_e, 0, 64)];
-    const float ex = lane < k ? expf(l[my_e] - lmax) : 0.f;
+    const float lmax = __shfl(my_l, 0, 64);
+    const float ex = lane < k ? expf(my_l - lmax) : 0.f;
     const float z = wave_sum(ex);
     if (lane < k) {
         idx[lane] = my_e;
@@ -64,11 +62,12 @@ __device__ void topk_wave(const float* l, int E, int k, int32_t* idx, float* w) 
     }
 }
 
-// grid (E, T), 64 threads. H = 256 * DV (float4 chunks lane + 64m).
+// grid (E, T), 64 threads: one wave per (expert row, token), H = 256 * DV
+// (lane reads float4 chunks lane + 64m), so the E x H fp32 router matrix
+// streams from HBM over the whole chip.
 template <int DV>
-__global__ __launch_bounds__(64) void k_route_split(const float* __restrict__ x, const float* __restrict__ Wr, int E,
-                                                    int k, float* __restrict__ logits, int32_t* __restrict__ idx,
-                                                    float* __restrict__ w, int* __restrict__ cnt) {
+__global__ __launch_bounds__(64) void k_route_logits(const float* __restrict__ x, const float* __restrict__ Wr, int E,
+                                                     float* __restrict__ logits) {
     constexpr int H = 256 * DV;
     const int lane = threadIdx.x, e = blockIdx.x, t = blockIdx.y;
     const f4v* xr = reinterpret_cast<const f4v*>(x + (size_t)t * H);
@@ -84,15 +83,14 @@ __global__ __launch_bounds__(64) void k_route_split(const float* __restrict__ x,
     }
     acc = wave_sum(acc);
     if (lane == 0) logits[(size_t)t * E + e] = acc;
-    __threadfence();
-    int prev = 0;
-    if (lane == 0) prev = atomicAdd(&cnt[t], 1);
-    prev = __shfl(prev, 0, 64);
-    if (prev == E - 1) {
-        __threadfence();
-        topk_wave(logits + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
-        if (lane == 0) cnt[t] = 0;
-    }
+}
+
+// grid T, 64 threads: the top-k of one token's logits (the kernel boundary
+// after k_route_logits makes every logit visible).
+__global__ __launch_bounds__(64) void k_route_topk(const float* __restrict__ logits, int E, int k,
+                                                   int32_t* __restrict__ idx, float* __restrict__ w) {
+    const float* lt = logits + (size_t)blockIdx.x * E;
+    topk_wave([&](int i) { return lt[i]; }, E, k, idx + (size_t)blockIdx.x * k, w + (size_t)blockIdx.x * k);
 }
 
 // grid T, 256 threads: one token per workgroup.
@@ -122,25 +120,27 @@ __global__ __launch_bounds__(256) void k_route_tokens(const float* __restrict__ 
     __syncthreads();
     if (logits_out)
         for (int e = tid; e < E; e += 256) logits_out[(size_t)t * E + e] = ls[e];
-    if (wave == 0) topk_wave(ls, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+    if (wave == 0) topk_wave([&](int i) { return ls[i]; }, E, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 hipError_t launch_route(int H, int E, int k, int T, const float* x, const float* Wr, int32_t* idx, float* w,
                         float* logits_out, void* ws, hipStream_t s) {
     char* base = reinterpret_cast<char*>(ws);
-    int* cnt = reinterpret_cast<int*>(base);
     const int DV = H / 256;
     if (T <= kRouteTicketMaxT) {
         float* lg = logits_out ? logits_out : reinterpret_cast<float*>(base + kCounterBytes);
         dim3 grid(E, T), block(64);
 #define RS(D) \
-    case D: hipLaunchKernelGGL((k_route_split<D>), grid, block, 0, s, x, Wr, E, k, lg, idx, w, cnt); break;
+    case D: hipLaunchKernelGGL((k_route_logits<D>), grid, block, 0, s, x, Wr, E, lg); break;
         switch (DV) {
             RS(1) RS(2) RS(3) RS(4) RS(5) RS(6) RS(7) RS(8) RS(9) RS(10) RS(11) RS(12) RS(13) RS(14) RS(15) RS(16)
             RS(17) RS(18) RS(19) RS(20) RS(21) RS(22) RS(23) RS(24) RS(25) RS(26) RS(27) RS(28) RS(29) RS(30) RS(31) RS(32)
             default: return hipErrorInvalidValue;
         }
 #undef RS
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_route_topk, dim3(T), dim3(64), 0, s, lg, E, k, idx, w);
     } else {
         dim3 grid(T), block(256);
 #define RT(D) \

@@ -95,6 +95,56 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (a + b) + (c + d);
 }
 
+// Max over all 64 lanes (uniform result).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dppf<0xB1>(v));
+    v = fmaxf(v, dppf<0x4E>(v));
+    v = fmaxf(v, dppf<0x141>(v));
+    v = fmaxf(v, dppf<0x140>(v));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off inside one kernel.
+// Data that one workgroup produces for another is written and read with
+// agent-scope atomic accesses, which the memory system keeps coherent across
+// the chip's XCDs (their L2s are not coherent with each other), and a
+// producer waits for its own stores to complete (s_waitcnt) before it bumps
+// a completion counter. This avoids agent-scope fences, whose L2 write-back
+// costs far more than the few kilobytes handed over here.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_agent(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Spin (bounded) until *cnt >= target. Returns false on timeout. The bound
+// (about 2^21 polls with a short sleep, tenths of a second) is far beyond
+// any legitimate wait and only ends a wait that could otherwise never end.
+__device__ __forceinline__ bool wait_count(const int* cnt, int target) {
+    for (int it = 0; it < (1 << 21); it++) {
+        if (ld_agent(cnt) >= target) return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
 
 }  // namespace moe

@@ -15,7 +15,12 @@ constexpr size_t kCounterBytes = 4096;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
-constexpr int kRouteTicketMaxT = 16;  // tokens routed with the split-row ticket kernel
+constexpr int kRouteTicketMaxT = 16;  // tokens routed by the split-row kernel
+// completion counters inside the counter region (int offsets)
+constexpr int kCntReady = 0;       // decode: gate/up tiles finished, per slot (<= 33)
+constexpr int kCntConsumed = 64;   // decode: down workgroups that read h, per slot
+constexpr int kCntDone = 128;      // decode: partial rows finished, per row block (<= 768)
+constexpr int kCntRoute = 1000;    // router: logit rows finished, per token (<= 16)
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 

@@ -208,3 +208,50 @@ def test_route_exact_logits_with_ties(m, orc, T):
     assert (gl == ol).all()
     assert (gi == oi).all()
     assert rel_err(gw, ow) <= TOL
+
+
+def test_one_workspace_across_layers_and_calls(m, orc):
+    """Route and decode of several layers share one workspace (its counters
+    must be back at zero after every call); each layer matches the oracle."""
+    wl = sg.get("qwen_decode")
+    E = 48
+    d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
+    n = max(m.moe_workspace_bytes(d, 1, m.MOE_MODE_ROUTE), m.moe_workspace_bytes(d, 1, m.MOE_MODE_DECODE))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for layer in range(3):
+        blocks = layer_blocks(wl, layer, E=E)
+        Wr = sg.router_weights(wl, layer, device="cuda")[:E].contiguous()
+        shared = [t.contiguous() for t in sg.shared_expert(wl, layer, device="cuda")]
+        x = sg.activations(wl, 2, layer, T=1, device="cuda").view(-1)
+        idx = torch.empty(wl.k, dtype=torch.int32, device="cuda")
+        w = torch.empty(wl.k, dtype=torch.float32, device="cuda")
+        y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            m.moe_route(d, x, 1, Wr, idx, w, None, ws)
+            m.moe_expert_decode(d, x, m.expert_ptr_table(blocks), idx, w, shared, y, ws)
+        torch.cuda.synchronize()
+        assert not ws[:4096].any(), "completion counters not reset"
+        _, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
+        assert (idx.cpu().numpy() == oi[0]).all()
+        hb = host_blocks(blocks, oi[0])
+        ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x.cpu().numpy(), [hb[int(e)] for e in oi[0]], ow[0],
+                                shared=[bf16_bits(s) for s in shared], nthreads=NTHREADS)
+        assert rel_err(y.cpu().numpy(), ref) <= TOL
+
+
+def test_expert_index_out_of_range_poisons_output(m):
+    """An expert index outside [0, E) is not dereferenced: the output turns
+    NaN instead (the host cannot check device-resident indices)."""
+    wl = sg.get("qwen_layer_decode")
+    E = 12
+    d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
+    blocks = layer_blocks(wl, 0, E=E)
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    x = sg.activations(wl, 0, 0, T=1, device="cuda").view(-1)
+    idx = torch.tensor([0, 1, 2, 3, 4, 5, 6, 7, 8, 15], dtype=torch.int32, device="cuda")
+    w = torch.full((wl.k,), 0.1, dtype=torch.float32, device="cuda")
+    y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    m.moe_expert_decode(d, x, m.expert_ptr_table(blocks), idx, w, None, y, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+    assert not ws[:4096].any()
