@@ -217,6 +217,87 @@ def run_decode(args, m, sg, torch):
     return res
 
 
+def prefill_flops_bytes(wl, idx, out_bf16):
+    """Algorithmic work of one prefill layer: 2 * (assignments) * 3 * H * I
+    flops; bytes = every expert that receives a token read once + x in + out."""
+    import numpy as np
+    n = idx.numel()
+    touched = int(np.unique(idx.cpu().numpy()).size)
+    flops = 2.0 * n * 3 * wl.H * wl.I
+    byts = touched * wl.block_bytes + wl.T * wl.H * 4 + wl.T * wl.H * (2 if out_bf16 else 4)
+    return flops, byts, touched
+
+
+def cpu_baseline_prefill(sg, wl, blocks, x, idx, w, budget_tokens=16):
+    import numpy as np
+    from oracle import oracle as O
+    O.build(force=False)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    toks = np.linspace(0, wl.T - 1, budget_tokens).astype(int)
+    ih = idx.cpu().numpy()[toks]
+    hb = {int(e): blocks[int(e)].cpu().numpy() for e in np.unique(ih)}
+    xh = x.cpu().numpy()[toks]
+    wh = w.cpu().numpy()[toks]
+    t0 = time.perf_counter()
+    O.moe_prefill(wl.fmt, wl.H, wl.I, wl.E, xh, hb, ih, wh, act=1 if wl.fmt == "nvfp4" else 2,
+                  out_bf16=wl.out_bf16, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(toks)} of {wl.T} prompt tokens (evenly spaced) through the layer with their "
+                      f"{wl.k} experts each, fp64, one thread per token, timed {dt:.1f} s"}
+
+
+def run_prefill(args, m, sg, torch):
+    wl = sg.get(args.workload)
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    t0 = time.time()
+    blocks = torch.empty((wl.E, wl.block_bytes), dtype=torch.uint8, device="cuda")
+    sg.fill_layer_blocks(wl, 0, blocks)
+    ptrs = m.expert_ptr_table(blocks)
+    x = sg.activations(wl, 0, 0, device="cuda")
+    idx, w = sg.routing(wl)
+    idx, w = idx.cuda(), w.cuda()
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16 if wl.out_bf16 else torch.float32, device="cuda")
+    ws = m.alloc_workspace(d, wl.T, m.MOE_MODE_PREFILL)
+    od = m.MOE_OUT_BF16 if wl.out_bf16 else m.MOE_OUT_F32
+    log(f"[bench] {wl.name}: {wl.E} experts resident ({blocks.numel() / 2**30:.2f} GiB), "
+        f"{wl.T} tokens, set up in {time.time() - t0:.1f} s")
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        m.moe_expert_prefill(d, x, wl.T, ptrs, idx, w, out, od, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        m.moe_expert_prefill(d, x, wl.T, ptrs, idx, w, out, od, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    flops, byts, touched = prefill_flops_bytes(wl, idx, wl.out_bf16)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbps = byts / (ms * 1e-3) / 1e9
+    mfma_peak = 2500.0 if wl.fmt == "nvfp4" else 10100.0
+    res = {
+        "metric": METRIC, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 MFMA, f32 accumulate" if wl.fmt == "nvfp4" else "mxfp4 MFMA, f32 accumulate",
+        "data": "synthetic (seeded SplitMix64; random-code FP4 experts, no trained weights)",
+        "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "intermediate": wl.I,
+                   "weights": wl.fmt, "tokens": wl.T, "assignments": int(idx.numel()), "experts_touched": touched,
+                   "routing": f"{wl.routing} (s={wl.zipf_s})" if wl.routing == "zipf" else wl.routing,
+                   "out": "bf16" if wl.out_bf16 else "f32", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "moe_expert_prefill (grouping + quantise + grouped GEMMs + combine)",
+                     "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": int(byts),
+                     "avg_us": round(ms * 1e3, 2)},
+        "mfma_TFLOPs": round(tflops, 2), "mfma_peak_TFLOPs": mfma_peak,
+        "mfma_frac": round(tflops / mfma_peak, 4), "flops_per_call": flops,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(sg, wl, blocks, x, idx, w)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,9 +320,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wl = sg.get(args.workload)
-    if wl.is_prefill:
-        raise SystemExit(f"workload {wl.name} is a prefill workload; not available in this bench yet")
-    res = run_decode(args, m, sg, torch)
+    res = run_prefill(args, m, sg, torch) if wl.is_prefill else run_decode(args, m, sg, torch)
     print(json.dumps(res), flush=True)
 
 

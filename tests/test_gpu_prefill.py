@@ -22,7 +22,10 @@ from gpu_helpers import NTHREADS, host_blocks, layer_blocks, rel_err
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
-TIE = 2.0 ** -16   # near-tie window, relative to the row's max |h| (fp32 accumulation error scale)
+# Near-tie window, relative to max |h| over the checked tokens: 2^-18 (3.8e-6)
+# is several times the fp32-accumulation difference between the GPU's h and
+# the oracle's fp64 h (measured <= 6e-7 of max |h| at every tested shape).
+TIE = 2.0 ** -18
 
 
 @pytest.fixture(scope="module")
@@ -108,17 +111,20 @@ def near_tie_mx(h, rowmax):
     return np.repeat(tie, 32, axis=-1).reshape(T, k, I), np.repeat(scale, 32, axis=-1).reshape(T, k, I)
 
 
-def check_outputs(orc, wl, hb, idx, w, o, gout):
-    """Per-token fp32 output check with the oracle-side near-tie allowance."""
+def check_outputs(orc, wl, hb, idx, w, o, gout, flips):
+    """Per-token fp32 output check with the oracle-side near-tie allowance;
+    every element where the GPU's h~ differs from the oracle's must be an
+    oracle near-tie."""
     T, k = idx.shape
     h_pre = o["h_pre"]
-    rowmax = np.abs(h_pre).max(axis=-1)
+    hmax = np.full(h_pre.shape[:2], np.abs(h_pre).max())
     if wl.fmt == "nvfp4":
-        tie = near_tie_bf16(h_pre, rowmax[..., None])
+        tie = near_tie_bf16(h_pre, hmax[..., None])
         step = bf16_steps(h_pre)
     else:
-        tie, scale = near_tie_mx(h_pre, rowmax)
+        tie, scale = near_tie_mx(h_pre, hmax)
         step = 2.0 * scale
+    assert not (flips & ~tie).any(), "h~ differs from the oracle away from a rounding near-tie"
     ref = o["out"]
     scale_all = np.abs(ref).max()
     nties = 0
@@ -179,9 +185,10 @@ def full_check(m, orc, wl, T, seed_layer=0, sample=None):
     # the GPU's own rounding step (bf16: checked against torch's conversion)
     if wl.fmt == "nvfp4":
         assert np.array_equal(gq, torch.tensor(gp).to(torch.bfloat16).float().numpy())
+    flip_mask = gq != hq
     nties = check_outputs(orc, wl, hb, idx.numpy()[toks], w.numpy()[toks], {"out": out, "h_pre": hp},
-                          g["out"][toks])
-    flips = int((gq != hq).sum())
+                          g["out"][toks], flip_mask)
+    flips = int(flip_mask.sum())
     print(f"{wl.name} T={T}: h err {e_h:.2e}, out err {rel_err(g['out'][toks], out):.2e}, "
           f"h~ flips {flips}, near-tie assignments {nties} of {len(toks) * k}")
     return g
