@@ -3,11 +3,16 @@
 Default workload: Qwen-shaped decode, 48 MoE layers x 512 NVFP4 experts
 (63.3 GiB resident in HBM) + one bf16 shared expert per layer, top-10, hidden
 2560, intermediate 640, one token per step with a fresh seeded activation
-vector per (step, layer). A step is one token through all 48 layers: per
-layer moe_route (router GEMV + softmax + top-k on the device) and
-moe_expert_decode (expert SwiGLU GEMVs + weighted combine + shared expert).
-The K timed steps are captured once as a HIP graph and replayed; inputs are
-resident in HBM before the timer starts.
+vector per (step, layer). A step is one token through all 48 layers: one
+moe_layer_decode per layer (router GEMV + softmax + top-k on the device,
+expert SwiGLU GEMVs, weighted combine, shared expert). The K timed steps are
+captured once as a HIP graph and replayed; inputs are resident in HBM before
+the timer starts.
+
+The roofline member covers the expert GEMV (moe_expert_decode: the gate/up
+and down kernels that stream the chosen experts' FP4 blocks): HIP events on
+the launch stream bracket each call while the GPU is still busy with a graph
+replay, so the host's enqueue time is not in the measured interval.
 
 Prints ONE JSON line (see the "roofline" and "cpu_baseline" members).
 """
@@ -16,6 +21,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -24,6 +30,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefill)"
+
+# HBM bytes per call of the roofline's kernels from rocprofv3 --pmc
+# (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain 1 GiB copy gives),
+# per workload; None until counters were taken on the current kernels.
+TRAFFIC: dict = {}
 
 
 def log(*a):
@@ -67,7 +78,6 @@ class DecodeModel:
         base = self.blocks.data_ptr()
         self.ptrs = torch.tensor([[base + (l * wl.E + e) * B for e in range(wl.E)] for l in range(self.L)],
                                  dtype=torch.int64, device="cuda")
-        self.ws_r = m.alloc_workspace(self.d, 1, m.MOE_MODE_ROUTE)
         self.ws_d = m.alloc_workspace(self.d, 1, m.MOE_MODE_DECODE)
         self.idx = torch.empty((self.L, wl.k), dtype=torch.int32, device="cuda")
         self.w = torch.empty((self.L, wl.k), dtype=torch.float32, device="cuda")
@@ -82,16 +92,14 @@ class DecodeModel:
         return torch.stack([torch.stack([sg.activations(wl, s, l % wl.layers, T=1, device="cuda").view(-1)
                                          for l in range(wl.layers)]) for s in range(steps)])
 
-    def layer(self, x, l, events=None):
-        m = self.m
-        if events is not None:
-            events[0].record()
-        m.moe_route(self.d, x, 1, self.Wr[l], self.idx[l], self.w[l], None, self.ws_r)
-        if events is not None:
-            events[1].record()
-        m.moe_expert_decode(self.d, x, self.ptrs[l], self.idx[l], self.w[l], self.shared[l], self.y[l], self.ws_d)
-        if events is not None:
-            events[2].record()
+    def layer(self, x, l):
+        self.m.moe_layer_decode(self.d, x, self.Wr[l], self.ptrs[l], self.shared[l], self.y[l], self.idx[l],
+                                self.w[l], self.ws_d)
+
+    def experts(self, x, l):
+        """The expert GEMV alone, on the routing the last layer call left."""
+        self.m.moe_expert_decode(self.d, x, self.ptrs[l], self.idx[l], self.w[l], self.shared[l], self.y[l],
+                                 self.ws_d)
 
     def step(self, xs, s, replica_offset=0):
         for l in range(self.wl.layers):
@@ -152,17 +160,7 @@ def run_decode(args, m, sg, torch):
         step(s)
     torch.cuda.synchronize()
 
-    # per-call timing with HIP events on the launch stream (eager launches)
-    nprobe = min(3 * wl.layers, 48) if wl.layers > 1 else 32
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nprobe)]
-    for i in range(nprobe):
-        s = W + (i // wl.layers) % K
-        l = i % wl.layers
-        model.layer(xs[s % (W + K), l], (i % nrep) * wl.layers + l if nrep > 1 else l, events=evs[i])
-    torch.cuda.synchronize()
-    route_us = sum(e[0].elapsed_time(e[1]) for e in evs) / nprobe * 1e3
-    expert_us = sum(e[1].elapsed_time(e[2]) for e in evs) / nprobe * 1e3
-
+    g = None
     if args.eager:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -188,6 +186,33 @@ def run_decode(args, m, sg, torch):
         elapsed = time.perf_counter() - t0
         mode = "hip_graph"
 
+    # Per-call durations with HIP events on the launch stream. The calls are
+    # enqueued behind a replay of the whole step graph (or a run of eager
+    # steps), so the GPU reaches each one with the next already queued.
+    nprobe = min(2 * wl.layers, 96) if wl.layers > 1 else 32
+    ev_x = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nprobe)]
+    ev_l = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nprobe)]
+
+    def probe(fn, evs):
+        if g is not None:
+            g.replay()
+        else:
+            for s in range(W, W + K):
+                step(s)
+        for i in range(nprobe):
+            l = i % wl.layers
+            li = (i % nrep) * wl.layers + l if nrep > 1 else l
+            evs[i][0].record()
+            fn(xs[W + (i // wl.layers) % K, l], li)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+
+    expert_samples = probe(model.experts, ev_x)
+    layer_samples = probe(model.layer, ev_l)
+    expert_us = statistics.median(expert_samples)
+    layer_us_call = statistics.median(layer_samples)
+
     ms_per_step = elapsed / K * 1e3
     tok_s = 1e3 / ms_per_step
     experts, router, shared, act = bytes_per_layer(wl)
@@ -203,13 +228,15 @@ def run_decode(args, m, sg, torch):
         "config": {"workload": wl.name, "layers": wl.layers, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
                    "intermediate": wl.I, "weights": wl.fmt, "shared_expert": "bf16" if wl.shared else None,
                    "tokens_per_step": 1, "replicas": replicas, "launch": mode, "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "moe_expert_decode (k_gateup + k_down)", "bound": "hbm",
+        "roofline": {"kernel": "expert GEMV: moe_expert_decode (k_gateup + k_down_combine)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": expert_call_bytes, "avg_us": round(expert_us, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": TRAFFIC.get(wl.name),
+                     "bytes_per_launch": expert_call_bytes, "median_us": round(expert_us, 3),
+                     "mean_us": round(statistics.fmean(expert_samples), 3), "samples": nprobe},
         "layer_us": round(ms_per_step * 1e3 / wl.layers, 3),
+        "layer_us_per_call": round(layer_us_call, 3),
+        "layer_GBps": round(layer_bytes / (ms_per_step * 1e-3 / wl.layers) / 1e9, 1),
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "route_us_eager": round(route_us, 3), "expert_us_eager": round(expert_us, 3),
         "hbm_copy_GBps_measured": round(copy_gbps, 1),
     }
     if not args.no_cpu_baseline:
@@ -307,6 +334,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="layer replicas to rotate through (cold timing)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run 4 device copies of 1 GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -319,6 +348,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        a = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 1 << 30, "copies": 4}), flush=True)
+        return
     wl = sg.get(args.workload)
     res = run_prefill(args, m, sg, torch) if wl.is_prefill else run_decode(args, m, sg, torch)
     print(json.dumps(res), flush=True)

@@ -22,7 +22,7 @@ FORMATS = {"nvfp4": MOE_FMT_NVFP4, "mxfp4": MOE_FMT_MXFP4}
 
 # every symbol declared in include/moe_fp4.h
 EXPORTS = ("moe_block_bytes", "moe_block_layout", "moe_workspace_bytes", "moe_route", "moe_expert_decode",
-           "moe_expert_prefill", "moe_dequant_block", "moe_status_string", "moe_last_error")
+           "moe_layer_decode", "moe_expert_prefill", "moe_dequant_block", "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -57,6 +57,8 @@ def _load():
     L.moe_route.restype = C.c_int; L.moe_route.argtypes = [D, P, I32, P, P, P, P, P, SZ, P]
     L.moe_expert_decode.restype = C.c_int
     L.moe_expert_decode.argtypes = [D, P, P, P, P, C.POINTER(moe_shared), P, P, SZ, P]
+    L.moe_layer_decode.restype = C.c_int
+    L.moe_layer_decode.argtypes = [D, P, P, P, C.POINTER(moe_shared), P, P, P, P, SZ, P]
     L.moe_expert_prefill.restype = C.c_int
     L.moe_expert_prefill.argtypes = [D, P, I32, P, P, P, P, I32, P, SZ, C.POINTER(moe_prefill_debug), P]
     L.moe_dequant_block.restype = C.c_int; L.moe_dequant_block.argtypes = [D, P, P, P, P, P]
@@ -120,6 +122,16 @@ def moe_expert_decode(d, x, expert_ptrs, idx, w, shared, y, ws, ws_bytes=None, s
     wsb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check(lib.moe_expert_decode(C.byref(d), _ptr(x), _ptr(expert_ptrs), _ptr(idx), _ptr(w), sh, _ptr(y), _ptr(ws),
                                  wsb, _stream(stream)))
+
+
+def moe_layer_decode(d, x, Wr, expert_ptrs, shared, y, idx_out, w_out, ws, ws_bytes=None, stream=None):
+    """shared: None or (gate, up, down) bf16 tensors."""
+    sh = None
+    if shared is not None:
+        sh = C.byref(moe_shared(_ptr(shared[0]), _ptr(shared[1]), _ptr(shared[2])))
+    wsb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(lib.moe_layer_decode(C.byref(d), _ptr(x), _ptr(Wr), _ptr(expert_ptrs), sh, _ptr(y), _ptr(idx_out),
+                                _ptr(w_out), _ptr(ws), wsb, _stream(stream)))
 
 
 def moe_expert_prefill(d, x, T, expert_ptrs, idx, w, out, out_dtype, ws, ws_bytes=None, dbg=None, stream=None):

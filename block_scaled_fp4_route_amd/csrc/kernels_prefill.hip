@@ -3,9 +3,9 @@
 // the whole prompt through each layer, so each expert's weights are read
 // once per prompt instead of once per chunk).
 //
-//  1. k_group_count / k_group_scatter: stable grouping of the T*k
-//     assignments a = t*k + j by expert (count, exclusive prefix sum, ordered
-//     compaction with ballots: deterministic, no atomics).
+//  1. k_group: stable grouping of the T*k assignments a = t*k + j by expert
+//     (count, exclusive prefix sum, ordered compaction with ballots:
+//     deterministic, no atomics).
 //  2. k_tile_list: M-tiles of every expert, heaviest experts first.
 //  3. k_quant_x_*: x~ = bf16(x) (NVFP4 layers) or MXFP4 per 32 (MXFP4 layers).
 //  4. ragged grouped GEMMs (gate/up with SiLU*mul epilogue, then down):
@@ -82,7 +82,7 @@ static PrefillWs prefill_layout(int fmt, int H, int I, int E, int k, int T, void
 bool prefill_supported(int fmt, int H, int I, int E, int k) {
     if (E < 1 || E > kMaxE || k < 1 || k > kMaxK) return false;
     if (fmt == kFmtNvfp4) return H % 256 == 0 && I % 128 == 0 && H <= 16384 && I <= 16384;
-    return H % 256 == 0 && I % 64 == 0 && H <= 16384 && I <= 16384;
+    return H % 512 == 0 && I % 64 == 0 && H <= 16384 && I <= 16384;
 }
 
 size_t prefill_ws_bytes(int fmt, int H, int I, int E, int k, int T) {
@@ -92,64 +92,63 @@ size_t prefill_ws_bytes(int fmt, int H, int I, int E, int k, int T) {
 // ---------------------------------------------------------------------------
 // 1. grouping
 
-__device__ __forceinline__ int block_sum_int(int v, int* red) {
-    // kGroupThreads threads; red has >= 16 ints
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    int s = 0;
-    for (int i = 0; i < kGroupThreads / 64; i++) s += red[i];
-    __syncthreads();
-    return s;
+    return v;
 }
 
-// grid E: count[e] = #{a : idx[a] == e}; also marks every pos[] invalid.
-__global__ __launch_bounds__(kGroupThreads) void k_group_count(const int32_t* __restrict__ idx, int n, int E,
-                                                               int* __restrict__ count, int* __restrict__ pos) {
-    __shared__ int red[16];
-    const int e = blockIdx.x;
-    int c = 0;
-    for (int a = threadIdx.x; a < n; a += kGroupThreads) c += idx[a] == e;
-    c = block_sum_int(c, red);
-    if (threadIdx.x == 0) count[e] = c;
-    const int lo = (int)((long long)n * e / E), hi = (int)((long long)n * (e + 1) / E);
-    for (int a = lo + threadIdx.x; a < hi; a += kGroupThreads) pos[a] = -1;
-}
-
-// grid E: off[e] = sum_{e'<e} count[e']; perm[off[e] + r] = the r-th
-// assignment (in increasing a) routed to e; pos[a] = its grouped position.
-__global__ __launch_bounds__(kGroupThreads) void k_group_scatter(const int32_t* __restrict__ idx, int n, int E,
-                                                                 const int* __restrict__ count, int* __restrict__ off,
-                                                                 int* __restrict__ perm, int* __restrict__ pos) {
-    __shared__ int red[16];
-    __shared__ int wtot[16];
+// grid E, 1024 threads per expert e, two passes over idx and no dependency
+// between workgroups: pass 1 counts lt = #{a : idx[a] < e} (= off[e], the
+// exclusive prefix sum of the counts) and eq = #{a : idx[a] == e}; pass 2
+// writes perm[off[e] + r] = the r-th assignment (in increasing a) routed to e
+// and pos[a] = its grouped position. Assignments whose expert index lies
+// outside [0, E) match no workgroup; workgroup e sets pos = -1 for those in
+// its slice of the array (a valid entry is only ever written by its expert's
+// workgroup, so the writes never collide).
+__global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ idx, int n, int E,
+                                                         int* __restrict__ count, int* __restrict__ off,
+                                                         int* __restrict__ perm, int* __restrict__ pos) {
+    __shared__ int red[2][kGroupThreads / 64];
+    __shared__ int wtot[kGroupThreads / 64];
     const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int s = 0;
-    for (int i = tid; i < e; i += kGroupThreads) s += count[i];
-    const int base = block_sum_int(s, red);
+    constexpr int NW = kGroupThreads / 64;
+    int lt = 0, eq = 0;
+    for (int a = tid; a < n; a += kGroupThreads) {
+        const int v = idx[a];
+        lt += (unsigned)v < (unsigned)e;
+        eq += v == e;
+    }
+    lt = wave_sum_int(lt);
+    eq = wave_sum_int(eq);
+    if (lane == 0) { red[0][wave] = lt; red[1][wave] = eq; }
+    __syncthreads();
+    int base = 0, cnt = 0;
+    for (int i = 0; i < NW; i++) { base += red[0][i]; cnt += red[1][i]; }
     if (tid == 0) {
         off[e] = base;
-        if (e == E - 1) off[E] = base + count[e];
+        count[e] = cnt;
+        if (e == E - 1) off[E] = base + cnt;
     }
-    int running = 0;
+    const int lo = (int)((long long)n * e / E), hi = (int)((long long)n * (e + 1) / E);
+    for (int a = lo + tid; a < hi; a += kGroupThreads)
+        if ((unsigned)idx[a] >= (unsigned)E) pos[a] = -1;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int running = base;
     for (int a0 = 0; a0 < n; a0 += kGroupThreads) {
         const int a = a0 + tid;
         const bool match = a < n && idx[a] == e;
         const unsigned long long m = __ballot(match);
-        const int lane_pre = __popcll(m & ((1ull << lane) - 1ull));
         if (lane == 0) wtot[wave] = __popcll(m);
         __syncthreads();
         int wave_pre = 0, total = 0;
-        for (int i = 0; i < kGroupThreads / 64; i++) {
+        for (int i = 0; i < NW; i++) {
             const int t = wtot[i];
             wave_pre += i < wave ? t : 0;
             total += t;
         }
         if (match) {
-            const int p = base + running + wave_pre + lane_pre;
+            const int p = running + wave_pre + __popcll(m & below);
             perm[p] = a;
             pos[a] = p;
         }
@@ -167,7 +166,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
     __shared__ int cnt[kMaxE];
     __shared__ int nt_sorted[kMaxE];
     __shared__ int ex_sorted[kMaxE];
-    __shared__ int start[kMaxE + 1];
+    __shared__ int start[kGroupThreads + 1];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += kGroupThreads) cnt[e] = count[e];
     __syncthreads();
@@ -179,15 +178,17 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
         nt_sorted[rank] = (c + BM - 1) / BM;
     }
     __syncthreads();
-    if (tid == 0) {
-        int s = 0;
-        for (int r = 0; r < E; r++) {
-            start[r] = s;
-            s += nt_sorted[r];
-        }
-        start[E] = s;
-        ntiles[0] = s;
+    // inclusive scan of nt_sorted (Hillis-Steele over kGroupThreads >= E entries)
+    int v = tid < E ? nt_sorted[tid] : 0;
+    for (int d = 1; d < kGroupThreads; d <<= 1) {
+        start[tid] = v;
+        __syncthreads();
+        if (tid >= d) v += start[tid - d];
+        __syncthreads();
     }
+    start[tid + 1] = v;          // start[r + 1] = tiles of ranks 0..r
+    if (tid == 0) start[0] = 0;
+    if (tid == kGroupThreads - 1) ntiles[0] = v;
     __syncthreads();
     for (int r = tid; r < E; r += kGroupThreads) {
         const int e = ex_sorted[r];
@@ -275,12 +276,28 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
 // Workgroup = (M-tile of 64 rows of one expert, 128 output columns of I).
 // Wave w owns output columns c0 = n0 + 32w .. +32 of BOTH gate and up, so its
 // B operand is 4 column blocks of 16 (gate c0, gate c0+16, up c0, up c0+16)
-// and SiLU*mul happens in registers. K runs over H in chunks of 128; within a
-// chunk lane group g = lane/16 owns K = 32g .. 32g+31 (one 16-byte load of 32
-// codes and 2 scale bytes per column block) and MFMA step s consumes its
-// elements 8s..8s+7, with the A operand read from LDS under the same
-// K mapping (the dot product is order-independent). The codes are decoded
-// to bf16 exactly (e2m1 x E4M3 has at most 6 significant bits).
+// and SiLU*mul happens in registers. K runs over H in chunks of 256; within a
+// chunk each lane group owns a contiguous quarter of K (see nv_kloop), with
+// the A operand read from LDS under the same K mapping (the dot product is
+// order-independent). The codes are decoded to bf16 exactly (e2m1 x E4M3 has
+// at most 6 significant bits).
+// Workgroup -> (M-tile, N-tile). Workgroups are dispatched round-robin over
+// the 8 XCDs (each with its own L2), so workgroup b runs on XCD b % 8. The
+// R = ntiles * NT real tiles are cut into 8 contiguous ranges, one per XCD,
+// in (M-tile, N-tile) order: the N-tiles of one M-tile (same gathered rows)
+// and the consecutive M-tiles of one expert (same weights) then share an L2.
+// Returns false for workgroups beyond the real tiles.
+__device__ __forceinline__ bool map_tile(int ntiles, int NT, int& tile, int& nt) {
+    const int R = ntiles * NT;
+    const int per = (R + 7) / 8;
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int L = x * per + j;
+    if (j >= per || L >= R) return false;
+    tile = L / NT;
+    nt = L % NT;
+    return true;
+}
+
 struct GemmArgs {
     const int* tile_e;
     const int* tile_m;
@@ -297,8 +314,6 @@ struct GemmArgs {
     int E, H, I, k, NT;     // NT = N-tiles per M-tile
 };
 
-constexpr int kALd = 128 + 8;  // LDS row stride (bf16) of an A tile: 128 K + 8 padding
-
 // Decode 8 e2m1 codes (dword d) times scale s to 8 bf16 (exact).
 __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
     const f2v a = fp4x2<0>(d), b = fp4x2<1>(d), c = fp4x2<2>(d), e = fp4x2<3>(d);
@@ -310,76 +325,95 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 }
 
 // Shared K loop of the two NVFP4 GEMMs: acc[rb][cb] += A[64 rows] x B[4
-// column blocks]^T over K (= KTOT) in chunks of 128. a_row(r) gives the
-// element offset of A row r (or -1 for a padding row); b_row(cb) the B
-// (weight) row of this lane's column in block cb; codes/scales are the
-// weight matrix regions with KTOT/2 code bytes and KTOT/16 scale bytes per row.
-template <class AROW>
-__device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, AROW a_row,
+// column blocks]^T over K (= KTOT) in chunks of BK (128 or 256). a_row(r)
+// gives the element offset of A row r (or -1 for a padding row); brow[cb] is
+// the weight row of this lane's column in block cb; codes/scales are the
+// weight matrix regions with KTOT/2 code bytes and KTOT/16 scale bytes per
+// row. Within a chunk, lane group g = lane/16 owns K = g*BK/4 .. +BK/4 (one
+// or two 16-byte code loads per column block, 2 or 4 scale bytes) and MFMA
+// step s consumes its elements 8s..8s+7; the A tile in LDS is read with the
+// same K mapping. The next chunk's loads are in flight during the current
+// chunk's MFMAs.
+template <int BK, class AROW>
+__device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, AROW a_row, int rows,
                                          const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scl,
                                          const int (&brow)[4], int KTOT, __bf16* lds) {
+    constexpr int LD = BK + 8;        // LDS row stride (bf16), padded
+    constexpr int QK = BK / 4;        // K per lane group (and per A-loader thread)
+    constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
+    constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
     const int tid = threadIdx.x, lane = tid & 63;
     const int g = lane >> 4, m16 = lane & 15;
-    // A loader: thread -> (row tid/4, 32-element quarter tid%4)
-    const int lr = tid >> 2, lq = tid & 3;
-    const int arow = a_row(lr);
-    const int nchunks = KTOT / 128;
-    uint4 anext[4];
-    uint4 bnext[4];
+    // A loader: 16-byte piece c = tid % CPR of rows tid / CPR + i * RPI: the
+    // lanes of one row read its BK*2 bytes contiguously, and in LDS 8
+    // consecutive lanes write 8 consecutive 16-byte slots (no bank conflicts
+    // with the odd 16-byte row stride).
+    constexpr int CPR = BK / 8;             // 16-byte pieces per row (16 or 32)
+    constexpr int RPI = 256 / CPR;          // rows per loader instruction (16 or 8)
+    constexpr int NA = 64 / RPI;            // loader instructions per chunk (4 or 8)
+    const int lc = tid % CPR, lr0 = tid / CPR;
+    int arow[NA];
+#pragma unroll
+    for (int i = 0; i < NA; i++) arow[i] = a_row(lr0 + i * RPI);
+    const int nchunks = KTOT / BK;
+    uint4 anext[NA];
+    uint4 bnext[4][NB];
     uint32_t snext[4];
     auto load_chunk = [&](int ch) {
-        const int k0 = ch * 128;
-        if (arow >= 0) {
-            const uint4* src = reinterpret_cast<const uint4*>(A + (size_t)arow + k0 + 32 * lq);
+        const int k0 = ch * BK;
 #pragma unroll
-            for (int i = 0; i < 4; i++) anext[i] = src[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; i++) anext[i] = uint4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < NA; i++)
+            anext[i] = arow[i] >= 0 ? *reinterpret_cast<const uint4*>(A + (size_t)arow[i] + k0 + 8 * lc)
+                                    : uint4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int cb = 0; cb < 4; cb++) {
             const size_t r = (size_t)brow[cb];
-            bnext[cb] = *reinterpret_cast<const uint4*>(codes + r * (KTOT / 2) + k0 / 2 + 16 * g);
-            snext[cb] = *reinterpret_cast<const uint16_t*>(scl + r * (KTOT / 16) + k0 / 16 + 2 * g);
+            const uint4* src = reinterpret_cast<const uint4*>(codes + r * (KTOT / 2) + k0 / 2 + (QK / 2) * g);
+#pragma unroll
+            for (int i = 0; i < NB; i++) bnext[cb][i] = src[i];
+            const uint8_t* sp = scl + r * (KTOT / 16) + k0 / 16 + (QK / 16) * g;
+            snext[cb] = NB == 1 ? (uint32_t) * reinterpret_cast<const uint16_t*>(sp)
+                                : *reinterpret_cast<const uint32_t*>(sp);
         }
     };
     auto store_a = [&](int buf) {
-        __bf16* dst = lds + (size_t)buf * 64 * kALd + lr * kALd + 32 * lq;
 #pragma unroll
-        for (int i = 0; i < 4; i++) reinterpret_cast<uint4*>(dst)[i] = anext[i];
+        for (int i = 0; i < NA; i++)
+            *reinterpret_cast<uint4*>(lds + (size_t)buf * 64 * LD + (lr0 + i * RPI) * LD + 8 * lc) = anext[i];
     };
     load_chunk(0);
     store_a(0);
     __syncthreads();
     for (int ch = 0; ch < nchunks; ch++) {
         const int cur = ch & 1;
-        uint4 bc[4];
+        uint4 bc[4][NB];
         uint32_t sc[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; cb++) { bc[cb] = bnext[cb]; sc[cb] = snext[cb]; }
-        if (ch + 1 < nchunks) load_chunk(ch + 1);
-        float s_lo[4], s_hi[4];
-#pragma unroll
         for (int cb = 0; cb < 4; cb++) {
-            s_lo[cb] = e4m3_to_f32(sc[cb] & 0xFFu);
-            s_hi[cb] = e4m3_to_f32(sc[cb] >> 8);
-        }
-        const __bf16* At = lds + (size_t)cur * 64 * kALd;
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
+            for (int i = 0; i < NB; i++) bc[cb][i] = bnext[cb][i];
+            sc[cb] = snext[cb];
+        }
+        if (ch + 1 < nchunks) load_chunk(ch + 1);
+        const __bf16* At = lds + (size_t)cur * 64 * LD;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
             bf16x8 bf[4];
 #pragma unroll
             for (int cb = 0; cb < 4; cb++) {
-                const uint32_t d = s == 0 ? bc[cb].x : (s == 1 ? bc[cb].y : (s == 2 ? bc[cb].z : bc[cb].w));
-                bf[cb] = dequant8_bf16(d, s < 2 ? s_lo[cb] : s_hi[cb]);
+                const uint4 q = bc[cb][s / 4];
+                const uint32_t d = (s & 3) == 0 ? q.x : ((s & 3) == 1 ? q.y : ((s & 3) == 2 ? q.z : q.w));
+                const float sv = e4m3_to_f32((sc[cb] >> (8 * (s / 2))) & 0xFFu);
+                bf[cb] = dequant8_bf16(d, sv);
             }
 #pragma unroll
             for (int rb = 0; rb < 4; rb++) {
-                const bf16x8 af = *reinterpret_cast<const bf16x8*>(At + (16 * rb + m16) * kALd + 32 * g + 8 * s);
+                if (16 * rb < rows) {  // uniform: skip padding row blocks of a short tile
+                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(At + (16 * rb + m16) * LD + QK * g + 8 * s);
 #pragma unroll
-                for (int cb = 0; cb < 4; cb++)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[cb], acc[rb][cb], 0, 0, 0);
+                    for (int cb = 0; cb < 4; cb++)
+                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[cb], acc[rb][cb], 0, 0, 0);
+                }
             }
         }
         if (ch + 1 < nchunks) store_a(cur ^ 1);
@@ -387,10 +421,13 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
     }
 }
 
+constexpr int kBKGate = 256;  // K chunk of the gate/up GEMM (K = H)
+constexpr int kBKDown = 128;  // K chunk of the down GEMM (K = I)
+
 __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * kALd];
-    const int tile = blockIdx.x / a.NT, nt = blockIdx.x % a.NT;
-    if (tile >= a.ntiles[0]) return;
+    __shared__ __bf16 lds[2 * 64 * (kBKGate + 8)];
+    int tile, nt;
+    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = min(kBM_NV, a.count[e] - m0);
     const int base = a.off[e] + m0;
@@ -411,7 +448,7 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop(acc, X, a_row, codes, scl, brow, H, lds);
+    nv_kloop<kBKGate>(acc, X, a_row, rows, codes, scl, brow, H, lds);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
     const int g = lane >> 4;
@@ -437,9 +474,9 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
 // 64 grouped rows, 256 columns of H); wave w owns columns n0 + 64w .. +64 as
 // 4 column blocks of 16. A rows are contiguous grouped rows of h~.
 __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * kALd];
-    const int tile = blockIdx.x / a.NT, nt = blockIdx.x % a.NT;
-    if (tile >= a.ntiles[0]) return;
+    __shared__ __bf16 lds[2 * 64 * (kBKDown + 8)];
+    int tile, nt;
+    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = min(kBM_NV, a.count[e] - m0);
     const int base = a.off[e] + m0;
@@ -458,7 +495,7 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop(acc, Hq, a_row, codes, scl, brow, I, lds);
+    nv_kloop<kBKDown>(acc, Hq, a_row, rows, codes, scl, brow, I, lds);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
@@ -474,75 +511,113 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // 4c. MXFP4 gate/up with the scaled FP4 MFMA (16x16x128): workgroup = (M-tile
-// of 32 rows = 2 row blocks, 64 output columns of I); wave w owns columns
-// n0 + 16w .. +16 of gate and up. Lane l holds row/column l%16 and
-// K = k0 + 32(l/16) .. +31: 16 code bytes plus one UE8M0 scale byte, read
-// straight from x~ and from the weight rows.
+// of 32 rows = 2 row blocks, 64*NCB output columns of I); wave w owns NCB
+// column blocks of 16 of gate and of up, so one activation fragment feeds
+// 2*NCB MFMAs. Lane l holds row/column l%16 and K = k0 + 32(l/16) .. +31:
+// 16 code bytes plus one UE8M0 scale byte, read straight from x~ and from
+// the weight rows. KU K-steps of loads are in flight ahead of the MFMAs.
+template <int NCB, int KU>
 __global__ __launch_bounds__(256) void k_gateup_mx(GemmArgs a) {
-    const int tile = blockIdx.x / a.NT, nt = blockIdx.x % a.NT;
-    if (tile >= a.ntiles[0]) return;
+    int tile, nt;
+    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = min(kBM_MX, a.count[e] - m0);
     const int base = a.off[e] + m0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I, k = a.k;
     const int g = lane >> 4, m16 = lane & 15;
-    const int c = nt * 64 + 16 * wave + m16;
+    const int cbase = nt * 64 * NCB + 16 * NCB * wave + m16;
     const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
-    const uint8_t* gcode = blk + (size_t)c * (H / 2);
-    const uint8_t* ucode = blk + (size_t)(I + c) * (H / 2);
-    const uint8_t* gscl = blk + (size_t)3 * I * H / 2 + (size_t)c * (H / 32);
-    const uint8_t* uscl = blk + (size_t)3 * I * H / 2 + (size_t)(I + c) * (H / 32);
+    const uint8_t* scl0 = blk + (size_t)3 * I * H / 2;
     const uint8_t* xc = reinterpret_cast<const uint8_t*>(a.a_src);
-    // A rows of the two row blocks (padding rows read row 0 of the tile: their
-    // outputs are discarded)
+    // A rows of the two row blocks (padding rows read row 0 of the tile:
+    // their outputs are discarded)
     int ar[2];
 #pragma unroll
     for (int rb = 0; rb < 2; rb++) {
         const int r = 16 * rb + m16;
         ar[rb] = a.perm[base + (r < rows ? r : 0)] / k;
     }
-    f32x4 acc[2][2];
+    const int nrb = rows > 16 ? 2 : 1;  // wave-uniform
+    f32x4 acc[2][2 * NCB];
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < H; k0 += 128) {
-        const int kb = k0 + 32 * g;
-        const uint4 bg = *reinterpret_cast<const uint4*>(gcode + kb / 2);
-        const uint4 bu = *reinterpret_cast<const uint4*>(ucode + kb / 2);
-        const int sg = gscl[kb / 32], su = uscl[kb / 32];
-        const i32x8 Bg = {(int)bg.x, (int)bg.y, (int)bg.z, (int)bg.w, 0, 0, 0, 0};
-        const i32x8 Bu = {(int)bu.x, (int)bu.y, (int)bu.z, (int)bu.w, 0, 0, 0, 0};
+    for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const uint4 av = *reinterpret_cast<const uint4*>(xc + (size_t)ar[rb] * (H / 2) + kb / 2);
-            const int sa = a.a_scl[(size_t)ar[rb] * (H / 32) + kb / 32];
-            const i32x8 A = {(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
-            acc[rb][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bg, acc[rb][0], 4, 4, 0, sa, 0, sg);
-            acc[rb][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bu, acc[rb][1], 4, 4, 0, sa, 0, su);
+        for (int j = 0; j < 2 * NCB; j++) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // B rows: j < NCB gate column blocks, j >= NCB up column blocks
+    uint4 bv[2][KU][2 * NCB], av[2][KU][2];
+    int sb[2][KU][2 * NCB], sa[2][KU][2];
+    auto load = [&](int buf, int kg) {
+#pragma unroll
+        for (int u = 0; u < KU; u++) {
+            const int kb = (kg + u) * 128 + 32 * g;
+#pragma unroll
+            for (int j = 0; j < 2 * NCB; j++) {
+                const size_t row = (size_t)(j < NCB ? 0 : I) + cbase + 16 * (j % NCB);
+                bv[buf][u][j] = *reinterpret_cast<const uint4*>(blk + row * (H / 2) + kb / 2);
+                sb[buf][u][j] = scl0[row * (H / 32) + kb / 32];
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                av[buf][u][rb] = *reinterpret_cast<const uint4*>(xc + (size_t)ar[rb] * (H / 2) + kb / 2);
+                sa[buf][u][rb] = a.a_scl[(size_t)ar[rb] * (H / 32) + kb / 32];
+            }
         }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < KU; u++) {
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                if (rb < nrb) {  // uniform: skip the padding row block of a short tile
+                    const uint4 v = av[buf][u][rb];
+                    const i32x8 A = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+#pragma unroll
+                    for (int j = 0; j < 2 * NCB; j++) {
+                        const uint4 w = bv[buf][u][j];
+                        const i32x8 B = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+                        acc[rb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[rb][j], 4, 4, 0,
+                                                                                      sa[buf][u][rb], 0, sb[buf][u][j]);
+                    }
+                }
+            }
+        }
+    };
+    const int nsteps = H / 128;  // multiple of 2*KU (H % 512 == 0 is required, KU <= 2)
+    // two K groups per iteration so that both register buffers have
+    // compile-time indices
+    load(0, 0);
+    for (int kg = 0; kg < nsteps; kg += 2 * KU) {
+        if (kg + KU < nsteps) load(1, kg + KU);
+        compute(0);
+        if (kg + KU >= nsteps) break;
+        if (kg + 2 * KU < nsteps) load(0, kg + 2 * KU);
+        compute(1);
     }
-    // D layout: lane holds column c, rows 16 rb + 4 g + i
+    // D layout: lane holds column cbase + 16 j, rows 16 rb + 4 g + i
     float* hf = reinterpret_cast<float*>(a.out);
 #pragma unroll
     for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r = 16 * rb + 4 * g + i;
-            if (r < rows) {
-                const float hv = silu_mul(acc[rb][0][i], acc[rb][1][i]);
-                const size_t o = (size_t)(base + r) * I + c;
-                hf[o] = hv;
-                if (a.h_pre) a.h_pre[o] = hv;
+        for (int j = 0; j < NCB; j++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = 16 * rb + 4 * g + i;
+                if (r < rows) {
+                    const float hv = silu_mul(acc[rb][j][i], acc[rb][NCB + j][i]);
+                    const size_t o = (size_t)(base + r) * I + cbase + 16 * j;
+                    hf[o] = hv;
+                    if (a.h_pre) a.h_pre[o] = hv;
+                }
             }
-        }
 }
 
 // 4d. MXFP4 down with the scaled FP4 MFMA (32x32x64): workgroup = (M-tile of
 // 32 grouped rows, 256 columns of H); wave w owns 2 column blocks of 32.
 // Lane l holds row/column l%32 and K = k0 + 32(l/32) .. +31.
 __global__ __launch_bounds__(256) void k_down_mx(GemmArgs a) {
-    const int tile = blockIdx.x / a.NT, nt = blockIdx.x % a.NT;
-    if (tile >= a.ntiles[0]) return;
+    int tile, nt;
+    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = min(kBM_MX, a.count[e] - m0);
     const int base = a.off[e] + m0;
@@ -560,19 +635,48 @@ __global__ __launch_bounds__(256) void k_down_mx(GemmArgs a) {
     for (int cb = 0; cb < 2; cb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[cb][i] = 0.f;
-    for (int k0 = 0; k0 < I; k0 += 64) {
-        const int kb = k0 + 32 * g;
-        const uint4 av = *reinterpret_cast<const uint4*>(hc + (size_t)arow * (I / 2) + kb / 2);
-        const int sa = a.a_scl[(size_t)arow * (I / 32) + kb / 32];
-        const i32x8 A = {(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
+    constexpr int KU = 5;  // I / 64 is a multiple of 5 for I = 2880; tails handled below
+    uint4 av[2][KU], bv[2][KU][2];
+    int sa[2][KU], sb[2][KU][2];
+    const int nsteps = I / 64;
+    auto load = [&](int buf, int kg) {
 #pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-            const size_t n = (size_t)n0 + 32 * cb + m32;
-            const uint4 bv = *reinterpret_cast<const uint4*>(dcode + n * (I / 2) + kb / 2);
-            const int sb = dscl[n * (I / 32) + kb / 32];
-            const i32x8 B = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
-            acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[cb], 4, 4, 0, sa, 0, sb);
+        for (int u = 0; u < KU; u++) {
+            const int st = min(kg + u, nsteps - 1);  // clamped: tail steps reload a valid step, not used
+            const int kb = st * 64 + 32 * g;
+            av[buf][u] = *reinterpret_cast<const uint4*>(hc + (size_t)arow * (I / 2) + kb / 2);
+            sa[buf][u] = a.a_scl[(size_t)arow * (I / 32) + kb / 32];
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+                const size_t n = (size_t)n0 + 32 * cb + m32;
+                bv[buf][u][cb] = *reinterpret_cast<const uint4*>(dcode + n * (I / 2) + kb / 2);
+                sb[buf][u][cb] = dscl[n * (I / 32) + kb / 32];
+            }
         }
+    };
+    auto compute = [&](int buf, int kg) {
+#pragma unroll
+        for (int u = 0; u < KU; u++) {
+            if (kg + u < nsteps) {
+                const uint4 v = av[buf][u];
+                const i32x8 A = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+#pragma unroll
+                for (int cb = 0; cb < 2; cb++) {
+                    const uint4 w = bv[buf][u][cb];
+                    const i32x8 B = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+                    acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[cb], 4, 4, 0, sa[buf][u], 0,
+                                                                              sb[buf][u][cb]);
+                }
+            }
+        }
+    };
+    load(0, 0);
+    for (int kg = 0; kg < nsteps; kg += 2 * KU) {
+        if (kg + KU < nsteps) load(1, kg + KU);
+        compute(0, kg);
+        if (kg + KU >= nsteps) break;
+        if (kg + 2 * KU < nsteps) load(0, kg + 2 * KU);
+        compute(1, kg + KU);
     }
     // D layout: lane holds column l%32; register i -> row 8(i/4) + 4(l/32) + i%4
     float* Y = reinterpret_cast<float*>(a.out);
@@ -623,6 +727,8 @@ __global__ __launch_bounds__(256) void k_combine_prefill(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
+static unsigned grid8(int n) { return (unsigned)((n + 7) / 8 * 8); }
+
 #define LAUNCH_CHECK()                              \
     do {                                            \
         hipError_t e_ = hipGetLastError();          \
@@ -639,9 +745,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     int* perm = dbg && dbg->perm ? dbg->perm : L.perm;
     int* off = dbg && dbg->off ? dbg->off : L.off;
 
-    hipLaunchKernelGGL(k_group_count, dim3(E), dim3(kGroupThreads), 0, s, idx, n, E, L.count, L.pos);
-    LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_group_scatter, dim3(E), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
+    hipLaunchKernelGGL(k_group, dim3(E), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
     LAUNCH_CHECK();
     hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, L.tile_e, L.tile_m, L.ntiles);
     LAUNCH_CHECK();
@@ -658,11 +762,11 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
                            reinterpret_cast<bf16x8*>(xq));
         LAUNCH_CHECK();
         ga.a_src = xq; ga.out = L.hq; ga.h_q = dbg ? dbg->h_q : nullptr; ga.NT = I / 128;
-        hipLaunchKernelGGL(k_gateup_nv, dim3(mt * ga.NT), dim3(256), 0, s, ga);
+        hipLaunchKernelGGL(k_gateup_nv, dim3(grid8(mt * ga.NT)), dim3(256), 0, s, ga);
         LAUNCH_CHECK();
         GemmArgs gd = ga;
         gd.a_src = L.hq; gd.out = L.Y; gd.h_pre = nullptr; gd.h_q = nullptr; gd.NT = H / 256;
-        hipLaunchKernelGGL(k_down_nv, dim3(mt * gd.NT), dim3(256), 0, s, gd);
+        hipLaunchKernelGGL(k_down_nv, dim3(grid8(mt * gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     } else {
         uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);
@@ -671,8 +775,14 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         hipLaunchKernelGGL(k_quant_mx, dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s, x, nbx,
                            reinterpret_cast<uint32_t*>(xc), xs, (float*)nullptr);
         LAUNCH_CHECK();
-        ga.a_src = xc; ga.a_scl = xs; ga.out = L.hf; ga.NT = I / 64;
-        hipLaunchKernelGGL(k_gateup_mx, dim3(mt * ga.NT), dim3(256), 0, s, ga);
+        ga.a_src = xc; ga.a_scl = xs; ga.out = L.hf;
+        if (I % 192 == 0) {
+            ga.NT = I / 192;
+            hipLaunchKernelGGL((k_gateup_mx<3, 1>), dim3(grid8(mt * ga.NT)), dim3(256), 0, s, ga);
+        } else {
+            ga.NT = I / 64;
+            hipLaunchKernelGGL((k_gateup_mx<1, 4>), dim3(grid8(mt * ga.NT)), dim3(256), 0, s, ga);
+        }
         LAUNCH_CHECK();
         uint8_t* hc = reinterpret_cast<uint8_t*>(L.hq);
         uint8_t* hs = hc + (size_t)n * I / 2;
@@ -682,7 +792,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         LAUNCH_CHECK();
         GemmArgs gd = ga;
         gd.a_src = hc; gd.a_scl = hs; gd.out = L.Y; gd.h_pre = nullptr; gd.NT = H / 256;
-        hipLaunchKernelGGL(k_down_mx, dim3(mt * gd.NT), dim3(256), 0, s, gd);
+        hipLaunchKernelGGL(k_down_mx, dim3(grid8(mt * gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     }
     hipLaunchKernelGGL(k_combine_prefill, dim3((H / 4 + 255) / 256, T), dim3(256), 0, s, L.Y, L.pos, w, k, H, out,

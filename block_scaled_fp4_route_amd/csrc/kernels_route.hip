@@ -16,52 +16,6 @@ size_t route_ws_bytes(int T, int E) { return kCounterBytes + align256((size_t)T 
 
 bool route_supported(int H, int E, int k) { return H % 256 == 0 && H <= 8192 && E >= 1 && E <= kMaxE && k >= 1 && k <= kMaxK && k <= E; }
 
-// Top-k of E <= 1024 logits by one full wave; writes idx[0..k) (larger logit
-// first, lower expert index first among equal logits) and the softmax
-// weights renormalised over the chosen k. LOAD(e) reads logit e. Each round
-// takes the wave maximum with DPP, then the lowest expert index holding it
-// via a ballot.
-template <class LOAD>
-__device__ void topk_wave(LOAD load, int E, int k, int32_t* idx, float* w) {
-    constexpr int NI = kMaxE / 64;
-    const int lane = threadIdx.x & 63;
-    const float NEG = -__builtin_inff();
-    float v[NI];
-#pragma unroll
-    for (int i = 0; i < NI; i++) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? load(e) + 0.0f : NEG;  // + 0 folds -0 onto +0
-    }
-    int my_e = 0;
-    float my_l = 0.f;
-    for (int j = 0; j < k; j++) {
-        float m = v[0];
-#pragma unroll
-        for (int i = 1; i < NI; i++) m = fmaxf(m, v[i]);
-        m = wave_max(m);
-        int e = -1;  // wave-uniform
-#pragma unroll
-        for (int i = 0; i < NI; i++) {
-            const unsigned long long mask = __ballot(v[i] == m);
-            if (e < 0 && mask) e = (__ffsll((long long)mask) - 1) + 64 * i;
-        }
-#pragma unroll
-        for (int i = 0; i < NI; i++)
-            if (lane + 64 * i == e) v[i] = NEG;
-        if (lane == j) {
-            my_e = e;
-            my_l = m;
-        }
-    }
-    const float lmax = __shfl(my_l, 0, 64);
-    const float ex = lane < k ? expf(my_l - lmax) : 0.f;
-    const float z = wave_sum(ex);
-    if (lane < k) {
-        idx[lane] = my_e;
-        w[lane] = ex / z;
-    }
-}
-
 // grid (E, T), 64 threads: one wave per (expert row, token), H = 256 * DV
 // (lane reads float4 chunks lane + 64m), so the E x H fp32 router matrix
 // streams from HBM over the whole chip.

@@ -90,7 +90,7 @@ size_t moe_workspace_bytes(const moe_desc* d, int32_t T, int32_t mode) {
     if (check_desc(d) != MOE_OK || T < 0) return 0;
     switch (mode) {
         case MOE_MODE_ROUTE: return moe::route_ws_bytes(T, d->E);
-        case MOE_MODE_DECODE: return moe::decode_ws_bytes(d->H, d->I, d->k);
+        case MOE_MODE_DECODE: return moe::decode_ws_bytes(d->H, d->I, d->k, d->E);
         case MOE_MODE_PREFILL: return moe::prefill_ws_bytes(d->format, d->H, d->I, d->E, d->k, T);
         default: return 0;
     }
@@ -127,16 +127,45 @@ int moe_expert_decode(const moe_desc* d, const float* x, const void* const* expe
             return r;
     }
     if (d->k > moe::kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k=%d exceeds %d", d->k, moe::kMaxK);
+    if (d->E > moe::kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds %d", d->E, moe::kMaxE);
     moe::DecodePlan plan;
     if (!moe::plan_decode(d->format, d->H, d->I, &plan))
         return fail(MOE_ERR_UNSUPPORTED, "no decode kernel for H=%d I=%d (needs H %% 512 == 0, H <= 4096, I <= 4096)",
                     d->H, d->I);
-    if ((r = check_ws(ws, ws_bytes, moe::decode_ws_bytes(d->H, d->I, d->k)))) return r;
+    if ((r = check_ws(ws, ws_bytes, moe::decode_ws_bytes(d->H, d->I, d->k, d->E)))) return r;
     return hip_status(moe::launch_decode(d->format, plan, d->E, d->H, d->I, d->k, x, expert_ptrs, idx, w,
                                          shared ? shared->gate : nullptr, shared ? shared->up : nullptr,
                                          shared ? shared->down : nullptr, y, ws,
                                          reinterpret_cast<hipStream_t>(stream)),
                       "decode launch");
+}
+
+int moe_layer_decode(const moe_desc* d, const float* x, const float* Wr, const void* const* expert_ptrs,
+                     const moe_shared* shared, float* y, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int r;
+    if ((r = check_desc(d))) return r;
+    if ((r = check_ptr(x, 16, "x")) || (r = check_ptr(Wr, 16, "Wr")) || (r = check_ptr(expert_ptrs, 8, "expert_ptrs")) ||
+        (r = check_ptr(y, 4, "y")) || (r = check_ptr(idx_out, 4, "idx_out")) || (r = check_ptr(w_out, 4, "w_out")))
+        return r;
+    if (shared) {
+        if ((r = check_ptr(shared->gate, 16, "shared->gate")) || (r = check_ptr(shared->up, 16, "shared->up")) ||
+            (r = check_ptr(shared->down, 16, "shared->down")))
+            return r;
+    }
+    if (!moe::route_supported(d->H, d->E, d->k))
+        return fail(MOE_ERR_UNSUPPORTED, "router needs H %% 256 == 0, H <= 8192, E <= %d, k <= %d (H=%d E=%d k=%d)",
+                    moe::kMaxE, moe::kMaxK, d->H, d->E, d->k);
+    moe::DecodePlan plan;
+    if (!moe::plan_decode(d->format, d->H, d->I, &plan))
+        return fail(MOE_ERR_UNSUPPORTED, "no decode kernel for H=%d I=%d (needs H %% 512 == 0, H <= 4096, I <= 4096)",
+                    d->H, d->I);
+    if ((r = check_ws(ws, ws_bytes, moe::decode_ws_bytes(d->H, d->I, d->k, d->E)))) return r;
+    return hip_status(moe::launch_layer_decode(d->format, plan, d->E, d->H, d->I, d->k, x, Wr, expert_ptrs,
+                                               shared ? shared->gate : nullptr, shared ? shared->up : nullptr,
+                                               shared ? shared->down : nullptr, y, idx_out, w_out, ws,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                      "layer decode launch");
 }
 
 int moe_expert_prefill(const moe_desc* d, const float* x, int32_t T, const void* const* expert_ptrs,

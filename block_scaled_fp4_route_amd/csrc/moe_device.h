@@ -110,41 +110,103 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// ---------------------------------------------------------------------------
-// Cross-workgroup hand-off inside one kernel.
-// Data that one workgroup produces for another is written and read with
-// agent-scope atomic accesses, which the memory system keeps coherent across
-// the chip's XCDs (their L2s are not coherent with each other), and a
-// producer waits for its own stores to complete (s_waitcnt) before it bumps
-// a completion counter. This avoids agent-scope fences, whose L2 write-back
-// costs far more than the few kilobytes handed over here.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(int* p, int v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_agent(const int* p) {
-    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int add_agent(int* p, int v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until every memory access this wave issued has completed.
-__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+constexpr int kTopkMaxE = 1024;
 
-// Spin (bounded) until *cnt >= target. Returns false on timeout. The bound
-// (about 2^21 polls with a short sleep, tenths of a second) is far beyond
-// any legitimate wait and only ends a wait that could otherwise never end.
-__device__ __forceinline__ bool wait_count(const int* cnt, int target) {
-    for (int it = 0; it < (1 << 21); it++) {
-        if (ld_agent(cnt) >= target) return true;
-        __builtin_amdgcn_s_sleep(2);
+// Top-k of E <= 64 * NI logits by one full wave: afterwards lane j < k holds
+// the j-th chosen expert (larger logit first, lower expert index first among
+// equal logits) in my_e and its weight, the softmax renormalised over the
+// chosen k, in my_w. LOAD(e) reads logit e (0 <= e < E).
+// Lane l holds experts l*NI .. l*NI + NI - 1, so among lanes holding the
+// round's maximum the lowest lane holds the lowest expert index. All loads
+// are issued before the first use (no load under a branch).
+// Non-finite logits can leave my_e outside [0, E); callers treat such an
+// index as invalid.
+template <int NI, class LOAD>
+__device__ __forceinline__ void topk_select_n(LOAD load, int E, int k, int& my_e, float& my_w) {
+    const int lane = threadIdx.x & 63;
+    const float NEG = -__builtin_inff();
+    float v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) v[i] = load(min(lane * NI + i, E - 1));
+#pragma unroll
+    for (int i = 0; i < NI; i++) v[i] = lane * NI + i < E ? v[i] + 0.0f : NEG;  // + 0 folds -0 onto +0
+    my_e = -1;
+    float my_l = 0.f;
+    for (int j = 0; j < k; j++) {
+        float m = v[0];
+#pragma unroll
+        for (int i = 1; i < NI; i++) m = fmaxf(m, v[i]);
+        m = wave_max(m);
+        int f = NI;  // first local slot holding the maximum
+#pragma unroll
+        for (int i = NI - 1; i >= 0; i--) f = v[i] == m ? i : f;
+        const unsigned long long b = __ballot(f < NI);
+        const int L = b ? __ffsll((long long)b) - 1 : 0;
+        const int fl = __builtin_amdgcn_readlane(f, L);
+        const int e = b ? L * NI + fl : -1;
+#pragma unroll
+        for (int i = 0; i < NI; i++) v[i] = (lane == L && i == fl) ? NEG : v[i];
+        if (lane == j) {
+            my_e = e;
+            my_l = m;
+        }
     }
-    return false;
+    const float lmax = __shfl(my_l, 0, 64);
+    const float ex = lane < k ? expf(my_l - lmax) : 0.f;
+    const float z = wave_sum(ex);
+    my_w = ex / z;
+}
+
+// topk_select_n with the smallest register count that holds E logits.
+template <class LOAD>
+__device__ __forceinline__ void topk_select(LOAD load, int E, int k, int& my_e, float& my_w) {
+    if (E <= 64)
+        topk_select_n<1>(load, E, k, my_e, my_w);
+    else if (E <= 128)
+        topk_select_n<2>(load, E, k, my_e, my_w);
+    else if (E <= 256)
+        topk_select_n<4>(load, E, k, my_e, my_w);
+    else if (E <= 512)
+        topk_select_n<8>(load, E, k, my_e, my_w);
+    else
+        topk_select_n<16>(load, E, k, my_e, my_w);
+}
+
+// As topk_select, writing idx[0..k) and w[0..k).
+template <class LOAD>
+__device__ __forceinline__ void topk_wave(LOAD load, int E, int k, int32_t* idx, float* w) {
+    int e;
+    float wt;
+    topk_select(load, E, k, e, wt);
+    const int lane = threadIdx.x & 63;
+    if (lane < k) {
+        idx[lane] = e;
+        w[lane] = wt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Buffer-resource loads over one expert block. The base address is made
+// wave-uniform (it lives in SGPRs), offsets are 32-bit byte offsets, and the
+// hardware returns 0 for any offset at or beyond `bytes` instead of reading
+// past the block. Word 3 (0x00020000) is the raw-buffer format of the gfx9
+// family.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(p)), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld_b32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld_b8(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
 }  // namespace moe

@@ -35,12 +35,17 @@ struct DecodePlan {
     int down_nrb;      // row blocks (H / RB)
 };
 bool plan_decode(int fmt, int H, int I, DecodePlan* p);
-size_t decode_ws_bytes(int H, int I, int k);
+size_t decode_ws_bytes(int H, int I, int k, int E);
 
 hipError_t launch_decode(int fmt, const DecodePlan& p, int E, int H, int I, int k, const float* x,
                          const void* const* expert_ptrs, const int32_t* idx, const float* w,
                          const uint16_t* sh_gate, const uint16_t* sh_up, const uint16_t* sh_down, float* y,
                          void* ws, hipStream_t s);
+
+hipError_t launch_layer_decode(int fmt, const DecodePlan& p, int E, int H, int I, int k, const float* x,
+                               const float* Wr, const void* const* expert_ptrs, const uint16_t* sh_gate,
+                               const uint16_t* sh_up, const uint16_t* sh_down, float* y, int32_t* idx_out,
+                               float* w_out, void* ws, hipStream_t s);
 
 // ---- router ----
 size_t route_ws_bytes(int T, int E);

@@ -141,8 +141,8 @@ int moe_route(const moe_desc *d, const float *x, int32_t T, const float *Wr, int
  * where expert_e(x) = down_e( silu(gate_e x) * (up_e x) ), silu(z) =
  * z / (1 + exp(-z)), weights decoded on the fly from the block at
  * expert_ptrs[e] (format per d->format), fp32 activations and fp32
- * accumulation. The sum over j runs in increasing j, so results are
- * bit-identical from run to run.
+ * accumulation. The combine runs in increasing j (then the shared
+ * expert), so results are bit-identical from run to run.
  *   x           [H] fp32, 16-B aligned
  *   expert_ptrs DEVICE array of E pointers (8-B aligned), each to one
  *               256-B-aligned expert block (resident layers:
@@ -150,10 +150,22 @@ int moe_route(const moe_desc *d, const float *x, int32_t T, const float *Wr, int
  *   idx [k] int32, w [k] fp32: the routing (e.g. from moe_route)
  *   shared      host struct of device pointers, or NULL
  *   y           [H] fp32 (out)
- * Requires H % 512 == 0, H <= 4096, I % 128 == 0 (NVFP4) or I % 32 == 0
- * (MXFP4), I <= 4096, k <= 32. */
+ * Requires H % 512 == 0, H <= 4096, 16 <= I <= 4096 (a multiple of G), and
+ * k <= 32; other shapes return MOE_ERR_UNSUPPORTED. */
 int moe_expert_decode(const moe_desc *d, const float *x, const void *const *expert_ptrs, const int32_t *idx,
                       const float *w, const moe_shared *shared, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* One decode layer in one call: moe_route (T = 1) followed by
+ * moe_expert_decode, with the same results (bit-identical chosen experts,
+ * weights and y), in three launches instead of four: the router GEMV shares
+ * a launch with the shared expert's gate/up (neither depends on the
+ * routing), and the top-k is recomputed at the start of every routed
+ * gate/up workgroup. idx_out [k] int32 and w_out [k] fp32 receive the
+ * routing. Requirements: those of moe_route and of moe_expert_decode;
+ * workspace: moe_workspace_bytes(d, 1, MOE_MODE_DECODE). */
+int moe_layer_decode(const moe_desc *d, const float *x, const float *Wr, const void *const *expert_ptrs,
+                     const moe_shared *shared, float *y, int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes,
+                     void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Prefill: T tokens grouped by expert                                     */
@@ -174,8 +186,8 @@ int moe_expert_decode(const moe_desc *d, const float *x, const void *const *expe
  * The combine runs in increasing j in fp32; out is fp32 [T][H] or, with
  * out_dtype = MOE_OUT_BF16, bf16 [T][H] rounded from that fp32 sum.
  *   x [T][H] fp32; idx, w [T][k]; expert_ptrs as for decode; dbg optional.
- * Requires H % 128 == 0 and I % 64 == 0 (NVFP4) or H % 128 == 0 and
- * I % 64 == 0 (MXFP4), k <= 32. */
+ * Requires H % 256 == 0 and I % 128 == 0 (NVFP4) or H % 512 == 0 and
+ * I % 64 == 0 (MXFP4), H and I <= 16384, E <= 1024, k <= 32. */
 int moe_expert_prefill(const moe_desc *d, const float *x, int32_t T, const void *const *expert_ptrs,
                        const int32_t *idx, const float *w, void *out, int32_t out_dtype, void *ws,
                        size_t ws_bytes, const moe_prefill_debug *dbg, void *stream);

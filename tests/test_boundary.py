@@ -71,7 +71,6 @@ def test_route_argument_errors():
 
 def test_decode_argument_errors():
     d = m.desc(2560, 640, 64, 10, "nvfp4")
-    ok = dict(x=FAKE, ptrs=FAKE, idx=FAKE, w=FAKE, y=FAKE)
     assert _err(m.moe_expert_decode, d, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
     assert _err(m.moe_expert_decode, d, FAKE, FAKE + 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, 0) == m.MOE_ERR_ARG
     assert _err(m.moe_expert_decode, d, FAKE, FAKE, FAKE, FAKE, (FAKE, None, FAKE), FAKE, FAKE, 1 << 20, 0) \
@@ -83,7 +82,30 @@ def test_decode_argument_errors():
     big_k = m.desc(2560, 640, 64, 40, "nvfp4")
     assert _err(m.moe_expert_decode, big_k, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 24, 0) \
         == m.MOE_ERR_UNSUPPORTED
-    del ok
+
+
+def test_layer_decode_argument_errors():
+    d = m.desc(2560, 640, 512, 10, "nvfp4")
+    need = m.moe_workspace_bytes(d, 1, m.MOE_MODE_DECODE)
+    args = [d, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need, 0]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return _err(m.moe_layer_decode, *a)
+
+    assert call(a1=None) == m.MOE_ERR_ARG           # x
+    assert call(a2=FAKE + 4) == m.MOE_ERR_ARG       # Wr misaligned
+    assert call(a3=None) == m.MOE_ERR_ARG           # expert_ptrs
+    assert call(a4=(FAKE, FAKE, None)) == m.MOE_ERR_ARG
+    assert call(a6=None) == m.MOE_ERR_ARG           # idx_out
+    assert call(a7=FAKE + 2) == m.MOE_ERR_ARG       # w_out misaligned
+    assert call(a9=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(a8=None, a9=0) == m.MOE_ERR_WORKSPACE
+    assert call(a0=m.desc(2560, 640, 2048, 10, "nvfp4"), a9=1 << 24) == m.MOE_ERR_UNSUPPORTED  # E > 1024
+    assert call(a0=m.desc(2560 + 256, 640, 512, 10, "nvfp4"), a9=1 << 24) == m.MOE_ERR_UNSUPPORTED  # H % 512
+    assert call(a0=m.desc(2560, 640, 512, 0, "nvfp4")) == m.MOE_ERR_ARG
 
 
 def test_status_strings():

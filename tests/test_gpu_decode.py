@@ -255,3 +255,113 @@ def test_expert_index_out_of_range_poisons_output(m):
     torch.cuda.synchronize()
     assert torch.isnan(y).all()
     assert not ws[:4096].any()
+
+
+# ----------------------------------------------------------- fused layer ---
+
+def _layer_inputs(wl, E, layer, step, with_shared):
+    blocks = layer_blocks(wl, layer, E=E)
+    Wr = sg.router_weights(wl, layer, device="cuda")[:E].contiguous()
+    shared = [t.contiguous() for t in sg.shared_expert(wl, layer, device="cuda")] if with_shared else None
+    x = sg.activations(wl, step, layer, T=1, device="cuda").view(-1)
+    return blocks, Wr, shared, x
+
+
+@pytest.mark.parametrize("name,E,with_shared", [
+    ("qwen_decode", 512, True),        # the full Qwen layer: 512 experts + shared expert
+    ("qwen_layer_decode", 64, False),
+    ("deepseek_decode", 384, False),   # the full DeepSeek layer
+    ("deepseek_decode", 40, True),     # MXFP4 with a (synthetic) shared expert
+])
+def test_layer_decode_parity_and_equal_to_two_calls(m, orc, name, E, with_shared):
+    """moe_layer_decode against the oracle (route, then the experts it chose),
+    and bit for bit against moe_route followed by moe_expert_decode."""
+    wl = sg.get(name)
+    blocks, Wr, shared, x = _layer_inputs(wl, E, 0, 3, with_shared)
+    d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
+    ptrs = m.expert_ptr_table(blocks)
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    idx = torch.full((wl.k,), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((wl.k,), -1.0, dtype=torch.float32, device="cuda")
+    m.moe_layer_decode(d, x, Wr, ptrs, shared, y, idx, w, ws)
+    # the two-call path on the same inputs
+    wsr = m.alloc_workspace(d, 1, m.MOE_MODE_ROUTE)
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    y2 = torch.empty_like(y)
+    m.moe_route(d, x, 1, Wr, idx2, w2, None, wsr)
+    m.moe_expert_decode(d, x, ptrs, idx2, w2, shared, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    assert not ws[:4096].any(), "completion counters not reset"
+
+    _, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
+    gi = idx.cpu().numpy()
+    assert (gi == oi[0]).all(), (gi, oi[0])
+    assert rel_err(w.cpu().numpy(), ow[0]) <= TOL
+    hb = host_blocks(blocks, gi)
+    sh = None if shared is None else [bf16_bits(s) for s in shared]
+    ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x.cpu().numpy(), [hb[int(e)] for e in gi], ow[0],
+                            shared=sh, nthreads=NTHREADS)
+    err = rel_err(y.cpu().numpy(), ref)
+    print(f"{name} E={E} shared={with_shared}: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL
+
+
+def test_layer_decode_many_layers_one_workspace(m, orc):
+    """Several layers enqueued back to back on one workspace with no host
+    synchronisation between them (each with its own seeded input); every
+    layer then matches the oracle and the counters are back at zero."""
+    wl = sg.get("qwen_decode")
+    E = 96
+    d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    layers = [_layer_inputs(wl, E, layer, 4, True) for layer in range(4)]
+    outs = []
+    for blocks, Wr, shared, x in layers:
+        y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(wl.k, dtype=torch.int32, device="cuda")
+        w = torch.empty(wl.k, dtype=torch.float32, device="cuda")
+        m.moe_layer_decode(d, x, Wr, m.expert_ptr_table(blocks), shared, y, idx, w, ws)
+        outs.append((y, idx))
+    torch.cuda.synchronize()
+    assert not ws[:4096].any()
+    for (blocks, Wr, shared, x), (y, idx) in zip(layers, outs):
+        xin = x.cpu().numpy()
+        _, oi, ow = orc.route(xin, Wr.cpu().numpy(), wl.k)
+        gi = idx.cpu().numpy()
+        assert (gi == oi[0]).all(), (gi, oi[0])
+        hb = host_blocks(blocks, gi)
+        ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, xin, [hb[int(e)] for e in gi], ow[0],
+                                shared=[bf16_bits(s) for s in shared], nthreads=NTHREADS)
+        assert rel_err(y.cpu().numpy(), ref) <= TOL
+
+
+def test_layer_decode_exact_router_ties(m, orc):
+    """Integer router weights with planted duplicate rows make the logits
+    exact and tied; the fused top-k must pick the oracle's experts (lower
+    index first among equals)."""
+    H, I, E, k = 512, 64, 48, 6
+    d = m.desc(H, I, E, k, "nvfp4")
+    wl = sg.Workload("ties", 91, H, I, E, k, "nvfp4", 1, 1, False, "router", 0.0, 0x18, 0x48, False)
+    blocks = layer_blocks(wl, 0)
+    g = torch.Generator().manual_seed(7)
+    Wr = torch.randint(-3, 4, (E, H), generator=g).float()
+    Wr[9] = Wr[2]
+    Wr[30] = Wr[2]
+    Wr[17] = Wr[44]
+    x = torch.randint(-2, 3, (H,), generator=g).float()
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    y = torch.empty(H, dtype=torch.float32, device="cuda")
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    w = torch.empty(k, dtype=torch.float32, device="cuda")
+    m.moe_layer_decode(d, x.cuda(), Wr.cuda(), m.expert_ptr_table(blocks), None, y, idx, w, ws)
+    torch.cuda.synchronize()
+    _, oi, ow = orc.route(x.numpy()[None], Wr.numpy(), k)
+    assert (idx.cpu().numpy() == oi[0]).all()
+    hb = host_blocks(blocks, oi[0])
+    ref, _ = orc.moe_decode("nvfp4", H, I, x.numpy(), [hb[int(e)] for e in oi[0]], ow[0], nthreads=NTHREADS)
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
