@@ -45,6 +45,11 @@ class moe_prefill_debug(C.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime (same soname as the system one). Loading
+    # torch first makes the library bind to that one, so the process holds a
+    # single runtime; loaded the other way round, the library's launches
+    # found no device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
                           "python block_scaled_fp4_route_amd/build.py")
@@ -151,7 +156,7 @@ def moe_dequant_block(d, block, gate, up, down, stream=None):
 # --- allocation helpers for callers (torch owns the memory) ----------------
 
 def alloc_workspace(d: moe_desc, T: int, mode: int, device="cuda"):
-    """A zero-filled workspace (the library needs its counters zero once)."""
+    """A workspace of the size the library asks for (zero-filled; any contents would do)."""
     import torch
     n = moe_workspace_bytes(d, T, mode)
     if n == 0:

@@ -4,19 +4,23 @@
 //  * gate/up tiles: gate and up rows of a chosen expert (or of the bf16
 //    shared expert) against the LDS-staged activation vector, SiLU*mul
 //    epilogue;
-//  * down tiles: for a block of 8 output rows, one wave per chosen expert
-//    (two for the shared expert) against that expert's hidden vector, then
-//    the weighted combine in fixed expert order in LDS;
-//  * for the fused layer entry point, the router rows share a launch with
-//    the shared expert's gate/up (neither depends on the routing), and the
-//    top-k runs redundantly at the start of every routed gate/up workgroup.
-// Kernel boundaries carry the remaining dependencies (router -> routed
-// gate/up -> down): on this chip they are cheaper than in-kernel
-// device-scope hand-offs between workgroups.
+//  * down items: a block of 8 output rows of one chosen expert (or of the
+//    shared expert) against its hidden vector, per wave; the down launch
+//    then forms the weighted combine in fixed expert order in LDS.
+// Fused layer entry point, three launches:
+//  1. router rows + the shared expert's gate/up (neither needs the routing);
+//  2. top-k, recomputed at the start of every routed gate/up workgroup,
+//     + the routed gate/up tiles + the shared expert's down rows (which
+//     stream from HBM while the top-k is being computed);
+//  3. routed down items + combine (adding the shared rows of launch 2).
+// Kernel boundaries carry the dependencies: on this chip they are cheaper
+// than in-kernel device-scope hand-offs between workgroups.
 // The kernels are latency-bound chains of dependent loads, so each level is
 // kept short: the expert pointer table is staged in LDS while the routing is
 // read, the gate/up launch hands the chosen blocks' addresses to the down
-// launch, and every weight load is issued before the first one is used.
+// launch, x is requested before the weights (the memory counter completes
+// in issue order, so a wait for x never waits for weights), and every weight
+// load of a wave is issued before the first one is used.
 // Weights are read with coalesced buffer loads (64 lanes x 4 B contiguous),
 // e2m1 pairs are converted by v_cvt_scalef32_pk_f32_fp4, the group scale is
 // applied once per 8 codes in registers, and rows are reduced with DPP.
@@ -28,10 +32,11 @@ namespace moe {
 constexpr int kMaxI = 4096;
 constexpr int kDownRB = 8;  // output rows per down workgroup
 
+// Workspace regions after the reserved bytes: h [(k+1)][I], logits [E],
+// chosen block addresses [k], shared-expert down rows [H].
 size_t decode_ws_bytes(int H, int I, int k, int E) {
-    (void)H;
     return kCounterBytes + align256((size_t)(k + 1) * I * sizeof(float)) + align256((size_t)E * sizeof(float)) +
-           align256((size_t)k * sizeof(void*));
+           align256((size_t)k * sizeof(void*)) + align256((size_t)H * sizeof(float));
 }
 
 bool plan_decode(int fmt, int H, int I, DecodePlan* p) {
@@ -69,18 +74,40 @@ struct DecodeArgs {
     float* w_out;            // [k]
     const void** sel;        // [k] block addresses of the chosen experts (NULL: invalid index)
     float* h;                // [(k+1)][I] SwiGLU hidden vectors (slot k = shared)
+    float* ysh;              // [H] shared expert's down rows (layer entry point)
     float* y;                // [H]
     int E, k, H, I;
     int has_shared;
     int gt_r;                // gate/up tiles per routed slot
     int gt_s;                // gate/up tiles of the shared slot
-    int n_items;             // down work items: k routed slots + 2 halves of the shared one
+    int n_items;             // down-launch items: k routed slots (+ 2 halves of the shared one)
+    int n_sd;                // shared-down workgroups in the top-k launch (layer entry point)
     uint32_t block_bytes;
 };
 
 __device__ __forceinline__ const void* valid_block(const DecodeArgs& a, const void* const* tbl, int e) {
     return (unsigned)e < (unsigned)a.E ? tbl[e] : nullptr;
 }
+
+// ----------------------------------------------------------------------------
+// x (K fp32) on its way to LDS: thread t of the workgroup's 256 loads float4
+// chunks t + 256u into registers (load), which are written to LDS later
+// (store), after the weight loads have been issued.
+template <int K>
+struct XStage {
+    static constexpr int N = (K / 4 + 255) / 256;
+    f4v t[N];
+    __device__ __forceinline__ void load(const float* x) {
+        const f4v* x4 = reinterpret_cast<const f4v*>(x);
+#pragma unroll
+        for (int u = 0; u < N; u++) t[u] = x4[min((int)threadIdx.x + 256 * u, K / 4 - 1)];
+    }
+    __device__ __forceinline__ void store(f4v* xs) const {
+#pragma unroll
+        for (int u = 0; u < N; u++)
+            if ((int)threadIdx.x + 256 * u < K / 4) xs[threadIdx.x + 256 * u] = t[u];
+    }
+};
 
 // ----------------------------------------------------------------------------
 // gate/up rows + SiLU*mul for one tile of a routed expert (block `blk`, NULL
@@ -90,19 +117,26 @@ __device__ __forceinline__ const void* valid_block(const DecodeArgs& a, const vo
 // 8(l+64m)..+7 whose activations it keeps in registers. Gate and up codes
 // ([I][H/2] each) are adjacent in the block, as are their scales; the bf16
 // shared expert uses the same lane/column map with 16-byte chunks.
+// xst holds this thread's part of x, already requested; every thread of the
+// workgroup calls this (it contains a barrier).
 template <int FMT, int D, int P, bool SHARED>
-__device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const void* blk, int pair0, f4v* xs) {
+__device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const void* blk, int pair0, f4v* xs,
+                                            const XStage<512 * D>& xst) {
     constexpr int K = 512 * D;     // H
     constexpr int KD = K / 8;      // code dwords per row (= 16-byte bf16 chunks per shared row)
     constexpr int G = Fmt<FMT>::G;
     constexpr int KS = K / G;      // scale bytes per row
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = threadIdx.x & 63;
     const int I = a.I;
     const int np = min(P, I - pair0);  // wave-uniform; <= 0 for idle waves of the last tile
     // an invalid expert index poisons this slot instead of reading anything
+    blk = uniform_ptr(blk);
     const bool bad = !SHARED && blk == nullptr;
 
-    // 1. weight loads first (they do not depend on x)
+    // 1. weight loads, unconditional (rows past the last are clamped onto it
+    // and their sums dropped; an invalid index gets a buffer of 0 bytes, whose
+    // loads return 0 without touching memory), so that the compiler's memory
+    // counter waits stay exact
     uint32_t wv[2 * P][D], sv[2 * P][D];
     uint4 v[2 * P][D];
     if (SHARED) {
@@ -110,41 +144,28 @@ __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const
         const uint4* uq = reinterpret_cast<const uint4*>(a.sh_up);
 #pragma unroll
         for (int r = 0; r < 2 * P; r++) {
-            const int p = r % P;
-            const size_t row = (size_t)pair0 + p;
-            if (p < np) {
+            const size_t row = (size_t)min(pair0 + r % P, I - 1);
 #pragma unroll
-                for (int m = 0; m < D; m++) v[r][m] = (r < P ? gq : uq)[row * KD + lane + 64 * m];
-            }
+            for (int m = 0; m < D; m++) v[r][m] = (r < P ? gq : uq)[row * KD + lane + 64 * m];
         }
-    } else if (!bad) {
-        const rsrc_t rb = make_rsrc(blk, a.block_bytes);
+    } else {
+        const rsrc_t rb = make_rsrc(bad ? (const void*)a.x : blk, bad ? 0u : a.block_bytes);
         const uint32_t scl = (uint32_t)3 * I * (K / 2);
 #pragma unroll
         for (int r = 0; r < 2 * P; r++) {
-            const int p = r % P;
-            const uint32_t row = (uint32_t)(r / P) * I + pair0 + p;
-            if (p < np) {
+            const uint32_t row = (uint32_t)(r / P) * I + min(pair0 + r % P, I - 1);
 #pragma unroll
-                for (int m = 0; m < D; m++) {
-                    const uint32_t c = lane + 64 * m;
-                    wv[r][m] = ld_b32(rb, row * (K / 2) + 4 * c);
-                    sv[r][m] = ld_b8(rb, scl + row * KS + c * 8 / G);
-                }
+            for (int m = 0; m < D; m++) {
+                const uint32_t c = lane + 64 * m;
+                wv[r][m] = ld_b32(rb, row * (K / 2) + 4 * c);
+                sv[r][m] = ld_b8(rb, scl + row * KS + c * 8 / G);
             }
         }
     }
 
-    // 2. x through LDS into registers: lane keeps columns 8(lane+64m)..+7
-    {
-        constexpr int NX = (K / 4 + 255) / 256;
-        f4v t[NX];
-#pragma unroll
-        for (int u = 0; u < NX; u++) t[u] = reinterpret_cast<const f4v*>(a.x)[min(tid + 256 * u, K / 4 - 1)];
-#pragma unroll
-        for (int u = 0; u < NX; u++)
-            if (tid + 256 * u < K / 4) xs[tid + 256 * u] = t[u];
-    }
+    // 2. x into LDS (it was requested before the weights), then registers:
+    // lane keeps columns 8(lane+64m)..+7
+    xst.store(xs);
     __syncthreads();
     if (np > 0) {
         float xr[8 * D];
@@ -159,25 +180,21 @@ __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const
 #pragma unroll
         for (int r = 0; r < 2 * P; r++) {
             float s = 0.f;
-            if (r % P < np) {
-                if (SHARED) {
+            if (SHARED) {
 #pragma unroll
-                    for (int m = 0; m < D; m++) {
-                        const float* xx = &xr[8 * m];
-                        s = fmaf(bf16_lo(v[r][m].x), xx[0], s); s = fmaf(bf16_hi(v[r][m].x), xx[1], s);
-                        s = fmaf(bf16_lo(v[r][m].y), xx[2], s); s = fmaf(bf16_hi(v[r][m].y), xx[3], s);
-                        s = fmaf(bf16_lo(v[r][m].z), xx[4], s); s = fmaf(bf16_hi(v[r][m].z), xx[5], s);
-                        s = fmaf(bf16_lo(v[r][m].w), xx[6], s); s = fmaf(bf16_hi(v[r][m].w), xx[7], s);
-                    }
-                } else if (!bad) {
-#pragma unroll
-                    for (int m = 0; m < D; m++)
-                        s = fmaf(scale_to_f32<FMT>(sv[r][m]), dot8_fp4(wv[r][m], &xr[8 * m]), s);
-                } else {
-                    s = __uint_as_float(0x7FC00000u);
+                for (int m = 0; m < D; m++) {
+                    const float* xx = &xr[8 * m];
+                    s = fmaf(bf16_lo(v[r][m].x), xx[0], s); s = fmaf(bf16_hi(v[r][m].x), xx[1], s);
+                    s = fmaf(bf16_lo(v[r][m].y), xx[2], s); s = fmaf(bf16_hi(v[r][m].y), xx[3], s);
+                    s = fmaf(bf16_lo(v[r][m].z), xx[4], s); s = fmaf(bf16_hi(v[r][m].z), xx[5], s);
+                    s = fmaf(bf16_lo(v[r][m].w), xx[6], s); s = fmaf(bf16_hi(v[r][m].w), xx[7], s);
                 }
+            } else {
+#pragma unroll
+                for (int m = 0; m < D; m++)
+                    s = fmaf(scale_to_f32<FMT>(sv[r][m]), dot8_fp4(wv[r][m], &xr[8 * m]), s);
             }
-            acc[r] = wave_sum(s);
+            acc[r] = bad ? __uint_as_float(0x7FC00000u) : wave_sum(s);
         }
         if (lane == 0) {
 #pragma unroll
@@ -192,7 +209,7 @@ __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const
 // float4 chunks lane + 64m (H = 256 * DV).
 template <int DV>
 __device__ __forceinline__ void router_rows(const DecodeArgs& a, int wg) {
-    const int lane = threadIdx.x & 63, e = 4 * wg + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, e = 4 * wg + wave_id();
     if (e >= a.E) return;
     const f4v* xr = reinterpret_cast<const f4v*>(a.x);
     const f4v* wr = reinterpret_cast<const f4v*>(a.Wr + (size_t)e * (256 * DV));
@@ -210,106 +227,198 @@ __device__ __forceinline__ void router_rows(const DecodeArgs& a, int wg) {
 }
 
 // ----------------------------------------------------------------------------
-// Down projection of one block of kDownRB output rows, all slots, and the
-// combine. Work item j < k: routed slot j, all rows; items k, k+1: the two
-// halves of the rows of the bf16 shared expert (its rows carry 3.5x the bytes
-// of an FP4 row). Wave v processes items v, v + nwaves, ... A row is covered
-// by L lanes (64/L rows per pass); lane s of a row reads code dwords s + L*m
-// (m < D, while < I/8) and holds the matching 8D hidden values. Partial rows
-// meet in LDS; thread r then forms y[row] = sum_j w[j] * part[j][r]
-// (+ shared) in increasing j.
-template <int FMT, int L, int D>
-__device__ __forceinline__ void down_rows(const DecodeArgs& a, int rb, float (*part)[kDownRB], float* wsh) {
+// Down projection, one wave, one item: passes q0 .. q0+nq-1 of row block rb
+// (kDownRB rows) of one matrix -- a routed FP4 block (`blk`, NULL for an
+// invalid index) or the bf16 shared down -- against h[slot]. A row is
+// covered by L lanes (RPW = 64/L rows per pass, pass q holds rows
+// rb*kDownRB + grp + q*RPW); lane s of a row reads code dwords s + L*m
+// (m < D, while < I/8) and the matching 8 hidden values per dword. The row
+// sum of pass q goes to dst[grp + q*RPW] (LDS or global).
+// The hidden vector is held in registers, or (hs != NULL) staged in this
+// wave's own LDS slice of I floats and read back per column chunk, which
+// frees 8D registers.
+template <int FMT, int L, int D, bool SHARED, bool HL>
+__device__ __forceinline__ void down_item(const DecodeArgs& a, int slot, const void* blk, int rb, int q0, int nq,
+                                          float* dst, f4v* hs) {
     constexpr int G = Fmt<FMT>::G;
     constexpr int RPW = 64 / L;               // rows per wave pass
     constexpr int PASSES = kDownRB / RPW;     // passes for all rows of the block
-    constexpr int QC = PASSES < 4 ? PASSES / 2 : (D >= 7 ? 2 : 4);  // passes per load group (divides PASSES / 2)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int H = a.H, I = a.I, k = a.k;
+    // passes per load group: it divides nq (all PASSES passes for a routed
+    // item, PASSES / 2 for a shared half item), and the shared expert's
+    // 16-byte bf16 chunks hold 4x the registers of the FP4 dwords
+    constexpr int QC = SHARED ? (PASSES < 4 ? PASSES / 2 : (D >= 7 ? 1 : 2))
+                              : (PASSES < 4 ? PASSES : (D >= 7 ? 2 : 4));
+    const int lane = threadIdx.x & 63;
+    const int H = a.H, I = a.I;
     const int KD = I / 8, KS = I / G;
     const int grp = lane / L, s = lane % L;
-    // the combine weights, read while the weights stream
-    if (tid < k) wsh[tid] = a.w[tid];
-    for (int item = wave; item < a.n_items; item += nwaves) {
-        const bool shared = item >= k;
-        const int slot = shared ? k : item;
-        const int q0 = shared ? (item - k) * (PASSES / 2) : 0;
-        const int nq = shared ? PASSES / 2 : PASSES;  // PASSES is even (2 or 8)
-        const void* blk = shared ? nullptr : a.sel[slot];
-        const bool bad = !shared && blk == nullptr;
-        const int row0 = rb * kDownRB + grp;  // row of pass q: row0 + q * RPW
-        // the hidden vector of this item's slot, in registers
-        float hr[8 * D];
-        const f4v* hp = reinterpret_cast<const f4v*>(a.h + (size_t)slot * I);
+    blk = uniform_ptr(blk);
+    const bool bad = !SHARED && blk == nullptr;
+    const int row0 = rb * kDownRB + grp;
+    // the hidden vector of this item's slot (zero past the row's end); every
+    // global load below is unconditional, with indices clamped, so that the
+    // compiler's memory counter waits stay exact
+    const f4v* hp = reinterpret_cast<const f4v*>(a.h + (size_t)slot * I);
+    float hr[HL ? 1 : 8 * D];
+    if constexpr (HL) {
+        constexpr int NU = (2 * L * D + 63) / 64;  // float4 chunks per lane (I/4 <= 2*L*D)
+        f4v t[NU];
+#pragma unroll
+        for (int u = 0; u < NU; u++) t[u] = hp[min(lane + 64 * u, 2 * KD - 1)];
+#pragma unroll
+        for (int u = 0; u < NU; u++)
+            if (lane + 64 * u < 2 * KD) hs[lane + 64 * u] = t[u];
+    } else {
 #pragma unroll
         for (int m = 0; m < D; m++) {
-            const int c = s + L * m;
-            f4v p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
-            if (c < KD) { p0 = hp[2 * c]; p1 = hp[2 * c + 1]; }
+            const int c = min(s + L * m, KD - 1);
+            const f4v p0 = hp[2 * c], p1 = hp[2 * c + 1];
             hr[8 * m + 0] = p0.x; hr[8 * m + 1] = p0.y; hr[8 * m + 2] = p0.z; hr[8 * m + 3] = p0.w;
             hr[8 * m + 4] = p1.x; hr[8 * m + 5] = p1.y; hr[8 * m + 6] = p1.z; hr[8 * m + 7] = p1.w;
         }
-        const rsrc_t rbuf = make_rsrc(blk, bad || shared ? 0u : a.block_bytes);
-        const uint32_t codes = (uint32_t)I * H;  // after gate, up
-        const uint32_t scl = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / G;
-        const uint4* dq = reinterpret_cast<const uint4*>(a.sh_down);
-        // passes in groups of QC (bounded registers), all loads of a group first
-        for (int qc = 0; qc < nq; qc += QC) {
-            uint32_t wv[QC][D], sv[QC][D];
-            uint4 v[QC][D];
+    }
+    // an invalid index gets a buffer of 0 bytes: its loads return 0 without
+    // touching memory, and its rows are poisoned below
+    const rsrc_t rbuf = make_rsrc(SHARED || bad ? (const void*)a.x : blk, SHARED || bad ? 0u : a.block_bytes);
+    const uint32_t codes = (uint32_t)I * H;  // after gate, up
+    const uint32_t scl = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / G;
+    const uint4* dq = reinterpret_cast<const uint4*>(a.sh_down);
+    // passes in groups of QC (bounded registers), all loads of a group first
+    for (int qc = 0; qc < nq; qc += QC) {
+        uint32_t wv[QC][D], sv[QC][D];
+        uint4 v[QC][D];
 #pragma unroll
-            for (int q = 0; q < QC; q++) {
-                const uint32_t row = (uint32_t)row0 + (q0 + qc + q) * RPW;
-                if (shared) {
+        for (int q = 0; q < QC; q++) {
+            const uint32_t row = (uint32_t)row0 + (q0 + qc + q) * RPW;
 #pragma unroll
-                    for (int m = 0; m < D; m++)
-                        if (s + L * m < KD) v[q][m] = dq[(size_t)row * KD + s + L * m];
-                } else if (!bad) {
-#pragma unroll
-                    for (int m = 0; m < D; m++) {
-                        const uint32_t c = s + L * m;
-                        if (c < (uint32_t)KD) {
-                            wv[q][m] = ld_b32(rbuf, codes + row * (I / 2) + 4 * c);
-                            sv[q][m] = ld_b8(rbuf, scl + row * KS + c * 8 / G);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < QC; q++) {
-                float acc = 0.f;
-                if (shared) {
-#pragma unroll
-                    for (int m = 0; m < D; m++) {
-                        if (s + L * m < KD) {
-                            const float* xx = &hr[8 * m];
-                            const uint4 t = v[q][m];
-                            acc = fmaf(bf16_lo(t.x), xx[0], acc); acc = fmaf(bf16_hi(t.x), xx[1], acc);
-                            acc = fmaf(bf16_lo(t.y), xx[2], acc); acc = fmaf(bf16_hi(t.y), xx[3], acc);
-                            acc = fmaf(bf16_lo(t.z), xx[4], acc); acc = fmaf(bf16_hi(t.z), xx[5], acc);
-                            acc = fmaf(bf16_lo(t.w), xx[6], acc); acc = fmaf(bf16_hi(t.w), xx[7], acc);
-                        }
-                    }
-                } else if (!bad) {
-#pragma unroll
-                    for (int m = 0; m < D; m++)
-                        if (s + L * m < KD)
-                            acc = fmaf(scale_to_f32<FMT>(sv[q][m]), dot8_fp4(wv[q][m], &hr[8 * m]), acc);
+            for (int m = 0; m < D; m++) {
+                const uint32_t c = min(s + L * m, KD - 1);
+                if (SHARED) {
+                    v[q][m] = dq[(size_t)row * KD + c];
                 } else {
-                    acc = __uint_as_float(0x7FC00000u);
+                    wv[q][m] = ld_b32(rbuf, codes + row * (I / 2) + 4 * c);
+                    sv[q][m] = ld_b8(rbuf, scl + row * KS + c * 8 / G);
                 }
-                const float r = (L == 16) ? row16_sum(acc) : wave_sum(acc);
-                if (s == 0) part[slot][grp + (q0 + qc + q) * RPW] = r;
             }
         }
+        float acc[QC];
+#pragma unroll
+        for (int q = 0; q < QC; q++) acc[q] = 0.f;
+        // per column chunk m: its 8 hidden values, then every pass of the group
+        // (each pass still accumulates over m in increasing order)
+#pragma unroll
+        for (int m = 0; m < D; m++) {
+            const bool in = s + L * m < KD;  // columns past the row's end leave acc unchanged
+            float xx[8];
+            if constexpr (HL) {
+                const int c = min(s + L * m, KD - 1);
+                const f4v p0 = hs[2 * c], p1 = hs[2 * c + 1];
+                xx[0] = p0.x; xx[1] = p0.y; xx[2] = p0.z; xx[3] = p0.w;
+                xx[4] = p1.x; xx[5] = p1.y; xx[6] = p1.z; xx[7] = p1.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; i++) xx[i] = hr[8 * m + i];
+            }
+#pragma unroll
+            for (int q = 0; q < QC; q++) {
+                float t = acc[q];
+                if (SHARED) {
+                    const uint4 u = v[q][m];
+                    t = fmaf(bf16_lo(u.x), xx[0], t); t = fmaf(bf16_hi(u.x), xx[1], t);
+                    t = fmaf(bf16_lo(u.y), xx[2], t); t = fmaf(bf16_hi(u.y), xx[3], t);
+                    t = fmaf(bf16_lo(u.z), xx[4], t); t = fmaf(bf16_hi(u.z), xx[5], t);
+                    t = fmaf(bf16_lo(u.w), xx[6], t); t = fmaf(bf16_hi(u.w), xx[7], t);
+                } else {
+                    t = fmaf(scale_to_f32<FMT>(sv[q][m]), dot8_fp4(wv[q][m], xx), t);
+                }
+                acc[q] = in ? t : acc[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < QC; q++) {
+            float r = (L == 16) ? row16_sum(acc[q]) : wave_sum(acc[q]);
+            if (bad) r = __uint_as_float(0x7FC00000u);
+            if (s == 0) dst[grp + (q0 + qc + q) * RPW] = r;
+        }
     }
-    __syncthreads();
-    if (tid < kDownRB) {
-        float acc = 0.f;
-        for (int j = 0; j < k; j++) acc = fmaf(wsh[j], part[j][tid], acc);
-        if (a.has_shared) acc += part[k][tid];
-        a.y[rb * kDownRB + tid] = acc;
+}
+
+// ----------------------------------------------------------------------------
+// Down projection of NJ routed items at once by one wave (16-lane rows, the
+// hidden vectors staged in the wave's LDS slices): the same rows, passes and
+// arithmetic as down_item for each item, with the loads of all items issued
+// before the first is used. Item j: slot[j], block blk[j] (NULL: invalid
+// index; an item with slot[j] < 0 is absent), row sums to dst[j].
+template <int FMT, int D, int NJ>
+__device__ __forceinline__ void down_items16(const DecodeArgs& a, const int (&slot)[NJ], const void* (&blk)[NJ],
+                                             int rb, float* const (&dst)[NJ], f4v* hs) {
+    constexpr int L = 16, G = Fmt<FMT>::G;
+    constexpr int RPW = 64 / L, PASSES = kDownRB / RPW;  // 4 rows per pass, 2 passes
+    const int lane = threadIdx.x & 63;
+    const int H = a.H, I = a.I;
+    const int KD = I / 8, KS = I / G;
+    const int grp = lane / L, s = lane % L;
+    const int row0 = rb * kDownRB + grp;
+    const uint32_t codes = (uint32_t)I * H;
+    const uint32_t scl = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / G;
+    bool bad[NJ];
+    rsrc_t rbuf[NJ];
+    // hidden vectors -> LDS (unconditional loads, clamped indices)
+    {
+        constexpr int NU = (2 * L * D + 63) / 64;
+        f4v t[NJ][NU];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const f4v* hp = reinterpret_cast<const f4v*>(a.h + (size_t)max(slot[j], 0) * I);
+#pragma unroll
+            for (int u = 0; u < NU; u++) t[j][u] = hp[min(lane + 64 * u, 2 * KD - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            blk[j] = uniform_ptr(blk[j]);
+            bad[j] = blk[j] == nullptr;
+            rbuf[j] = make_rsrc(bad[j] ? (const void*)a.x : blk[j], bad[j] ? 0u : a.block_bytes);
+#pragma unroll
+            for (int u = 0; u < NU; u++)
+                if (lane + 64 * u < 2 * KD) hs[j * (I / 4) + lane + 64 * u] = t[j][u];
+        }
+    }
+    uint32_t wv[NJ][PASSES][D], sv[NJ][PASSES][D];
+#pragma unroll
+    for (int j = 0; j < NJ; j++)
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const uint32_t row = (uint32_t)row0 + q * RPW;
+#pragma unroll
+            for (int m = 0; m < D; m++) {
+                const uint32_t c = min(s + L * m, KD - 1);
+                wv[j][q][m] = ld_b32(rbuf[j], codes + row * (I / 2) + 4 * c);
+                sv[j][q][m] = ld_b8(rbuf[j], scl + row * KS + c * 8 / G);
+            }
+        }
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        float acc[PASSES];
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) acc[q] = 0.f;
+#pragma unroll
+        for (int m = 0; m < D; m++) {
+            const bool in = s + L * m < KD;
+            const int c = min(s + L * m, KD - 1);
+            const f4v p0 = hs[j * (I / 4) + 2 * c], p1 = hs[j * (I / 4) + 2 * c + 1];
+            const float xx[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+            for (int q = 0; q < PASSES; q++) {
+                const float t = fmaf(scale_to_f32<FMT>(sv[j][q][m]), dot8_fp4(wv[j][q][m], xx), acc[q]);
+                acc[q] = in ? t : acc[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            float r = row16_sum(acc[q]);
+            if (bad[j]) r = __uint_as_float(0x7FC00000u);
+            if (s == 0 && slot[j] >= 0) dst[j][grp + q * RPW] = r;
+        }
     }
 }
 
@@ -338,19 +447,21 @@ template <int FMT, int GD, int GP>
 __global__ __launch_bounds__(256) void k_gateup(DecodeArgs a) {
     __shared__ f4v buf[1024];  // x, H <= 4096
     __shared__ const void* tbl[kMaxE];
-    const int bid = blockIdx.x, ng_r = a.k * a.gt_r, v = threadIdx.x >> 6;
+    const int bid = blockIdx.x, ng_r = a.k * a.gt_r, v = wave_id();
+    XStage<512 * GD> xst;
+    xst.load(a.x);
     if (bid < ng_r) {
         const int slot = bid / a.gt_r;
         const int e = a.idx[slot];
-        const int ej = (bid == 0 && (int)threadIdx.x < a.k) ? a.idx[threadIdx.x] : -1;
+        const int ej = a.idx[min((int)threadIdx.x, a.k - 1)];  // used by workgroup 0, lanes < k
         const void* t[kTableRegs];
         load_table(a, t);
         store_table(a, t, tbl);
         __syncthreads();
         if (bid == 0 && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, ej);
-        gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, e), ((bid % a.gt_r) * 4 + v) * GP, buf);
+        gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, e), ((bid % a.gt_r) * 4 + v) * GP, buf, xst);
     } else {
-        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (bid - ng_r) * 4 + v, buf);
+        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (bid - ng_r) * 4 + v, buf, xst);
     }
 }
 
@@ -359,73 +470,162 @@ template <int FMT, int GD>
 __global__ __launch_bounds__(256) void k_router_shared(DecodeArgs a) {
     __shared__ f4v buf[1024];
     const int nr = (a.E + 3) / 4;
-    if ((int)blockIdx.x < nr)
+    if ((int)blockIdx.x < nr) {
         router_rows<2 * GD>(a, blockIdx.x);
-    else
-        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (blockIdx.x - nr) * 4 + (threadIdx.x >> 6), buf);
+    } else {
+        XStage<512 * GD> xst;
+        xst.load(a.x);
+        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (blockIdx.x - nr) * 4 + wave_id(), buf, xst);
+    }
 }
 
-// moe_layer_decode, launch 2: every workgroup selects the top-k from the
-// logits (identically) while the pointer table is staged; workgroup 0
-// publishes the routing and the chosen blocks' addresses; then the routed
-// gate/up tiles.
-template <int FMT, int GD, int GP>
+// moe_layer_decode, launch 2. Routed workgroups: every one selects the top
+// slot+1 experts from the logits (the same selection rounds in every
+// workgroup, stopped once its own slot is known, so that early slots start
+// streaming early) while x and the pointer table arrive; the first
+// workgroup of the last slot, which runs all k rounds, publishes the
+// routing and the chosen blocks' addresses; then the routed gate/up tile. The last n_sd workgroups: the shared expert's
+// down rows into ysh, half a row block per wave (the same rows and passes
+// as the down launch's shared items).
+template <int FMT, int GD, int GP, int DL, int DD>
 __global__ __launch_bounds__(256) void k_topk_gateup(DecodeArgs a) {
     __shared__ f4v buf[1024];
     __shared__ const void* tbl[kMaxE];
     __shared__ int sel_e;
-    const int bid = blockIdx.x, slot = bid / a.gt_r;
+    const int bid = blockIdx.x, ng_r = a.k * a.gt_r;
+    if (bid >= ng_r) {
+        constexpr int PASSES = kDownRB / (64 / DL);
+        const int half = (bid - ng_r) * 4 + wave_id(), rb = half / 2;
+        if (rb * kDownRB < a.H)
+            down_item<FMT, DL, DD, true, false>(a, a.k, nullptr, rb, (half % 2) * (PASSES / 2), PASSES / 2,
+                                                a.ysh + rb * kDownRB, nullptr);
+        return;
+    }
+    const int slot = bid / a.gt_r;
+    XStage<512 * GD> xst;
+    xst.load(a.x);
     const void* t[kTableRegs];
     load_table(a, t);
+    const bool publisher = bid == (a.k - 1) * a.gt_r;
     int e = -1;
     float wt = 0.f;
     if (threadIdx.x < 64) {
-        topk_select([&](int i) { return a.logits[i]; }, a.E, a.k, e, wt);
+        topk_select([&](int i) { return a.logits[i]; }, a.E, slot + 1, e, wt);
         if ((int)threadIdx.x == slot) sel_e = e;
-        if (bid == 0 && (int)threadIdx.x < a.k) {
+        if (publisher && (int)threadIdx.x < a.k) {
             a.idx_out[threadIdx.x] = e;
             a.w_out[threadIdx.x] = wt;
         }
     }
     store_table(a, t, tbl);
     __syncthreads();
-    if (bid == 0 && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, e);
+    if (publisher && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, e);
     gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, sel_e),
-                                    ((bid % a.gt_r) * 4 + (threadIdx.x >> 6)) * GP, buf);
+                                    ((bid % a.gt_r) * 4 + wave_id()) * GP, buf, xst);
 }
 
 // down projection + combine (both entry points): one workgroup per block of
-// kDownRB output rows.
+// kDownRB output rows; wave v takes items v, v + nwaves, ... (item j < k:
+// routed slot j; items k, k+1: the two halves of the shared expert's rows,
+// present only when ysh is not used). Thread r then forms
+// y[row] = sum_j w[j] * part[j][r] (+ the shared row) in increasing j.
 // At most 16 waves (1024 threads, 128 VGPRs) where a wave's registers fit in
-// 128 (16-lane rows of up to 640 codes); otherwise 8 waves (512 threads, 256
-// VGPRs).
-constexpr int down_max_waves(int L, int D) { return (L == 16 && D <= 5) ? 16 : 8; }
+// 128 (16-lane rows of up to 640 codes); 4 waves (512 VGPRs) for the widest
+// rows (more than 3584 codes); otherwise 8 waves (512 threads, 256 VGPRs).
+constexpr int down_max_waves(int L, int D) { return (L == 16 && D <= 5) ? 16 : (D >= 8 ? 4 : 8); }
 
-template <int FMT, int DL, int DD>
+// SH: the shared expert's rows are items of this launch (moe_expert_decode)
+// rather than precomputed in ysh (moe_layer_decode). PAIRS (16-lane rows,
+// when the units fit the workgroup): one unit per wave, routed items two at
+// a time plus one wave per shared half, so that several small workgroups
+// share a CU and a launch covers the chip in one round. Otherwise waves loop
+// over single items.
+template <int FMT, int DL, int DD, bool SH, bool PAIRS>
 __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(DecodeArgs a) {
     __shared__ float part[kMaxK + 1][kDownRB];
     __shared__ float wsh[kMaxK];
-    down_rows<FMT, DL, DD>(a, blockIdx.x, part, wsh);
+    extern __shared__ f4v hsm[];  // 16-lane rows: hidden vectors, I-float slices per wave (dynamic size)
+    constexpr bool HL = DL == 16;
+    constexpr int PASSES = kDownRB / (64 / DL);
+    const int tid = threadIdx.x, wave = wave_id(), nwaves = blockDim.x >> 6;
+    const int rb = blockIdx.x, k = a.k;
+    // the combine's other inputs, requested while the weights stream
+    if (tid < k) wsh[tid] = a.w[tid];
+    const float ysh_row = (a.ysh != nullptr && tid < kDownRB) ? a.ysh[rb * kDownRB + tid] : 0.f;
+    if constexpr (PAIRS) {
+        // one unit per wave: routed items in pairs (items w and w + npair),
+        // then the two halves of the shared expert's rows; the wave's two LDS
+        // slices hold the hidden vectors
+        const int npair = (k + 1) / 2;
+        f4v* hs = hsm + (size_t)wave * 2 * (a.I / 4);
+        if (wave < npair) {
+            int sl[2] = {wave, wave + npair < k ? wave + npair : -1};
+            const void* bl[2] = {a.sel[sl[0]], sl[1] >= 0 ? a.sel[sl[1]] : nullptr};
+            float* const dd[2] = {part[sl[0]], part[max(sl[1], 0)]};
+            down_items16<FMT, DD, 2>(a, sl, bl, rb, dd, hs);
+        } else if (SH) {
+            down_item<FMT, DL, DD, true, true>(a, k, nullptr, rb, (wave - npair) * (PASSES / 2), PASSES / 2,
+                                               part[k], hs);
+        }
+    } else {
+        for (int item = wave; item < a.n_items; item += nwaves) {
+            f4v* hs = HL ? hsm + (size_t)wave * (a.I / 4) : nullptr;
+            if (!SH || item < k)
+                down_item<FMT, DL, DD, false, HL>(a, item, a.sel[item], rb, 0, PASSES, part[item], hs);
+            else
+                down_item<FMT, DL, DD, true, HL>(a, k, nullptr, rb, (item - k) * (PASSES / 2), PASSES / 2, part[k],
+                                                 hs);
+        }
+    }
+    __syncthreads();
+    if (tid < kDownRB) {
+        const int row = rb * kDownRB + tid;
+        float acc = 0.f;
+        for (int j = 0; j < k; j++) acc = fmaf(wsh[j], part[j][tid], acc);
+        if (a.has_shared) acc += a.ysh ? ysh_row : part[k][tid];
+        a.y[row] = acc;
+    }
 }
 
 // ----------------------------------------------------------------------------
 template <int FMT>
 static hipError_t launch_down(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
-    const int nw = min(down_max_waves(p.down_L, p.down_D), a.n_items);
+    const bool sh = a.n_items > a.k;
+    const int maxw = down_max_waves(p.down_L, p.down_D);
+    const int units = (a.k + 1) / 2 + (a.n_items - a.k);  // routed pairs + shared halves
+    const bool pairs = p.down_L == 16 && units <= maxw;
+    const int nw = pairs ? units : min(maxw, a.n_items);
     dim3 grid(a.H / kDownRB), block(64 * nw);
-#define DN(DL, DD) case DD: hipLaunchKernelGGL((k_down_combine<FMT, DL, DD>), grid, block, 0, s, a); break;
+    // hidden vectors in LDS for 16-lane rows: two I-float slices per wave
+    // (pairs), one otherwise
+    const size_t shm = p.down_L == 16 ? (size_t)nw * (pairs ? 2 : 1) * a.I * sizeof(float) : 0;
+#define DNV(DL, DD, SH, PR) hipLaunchKernelGGL((k_down_combine<FMT, DL, DD, SH, PR>), grid, block, shm, s, a)
+#define DN(DL, DD)                                                   \
+    case DD:                                                         \
+        if (pairs) {                                                 \
+            if (sh) DNV(DL, DD, true, true); else DNV(DL, DD, false, true);   \
+        } else {                                                     \
+            if (sh) DNV(DL, DD, true, false); else DNV(DL, DD, false, false); \
+        }                                                            \
+        break;
     if (p.down_L == 16) {
         switch (p.down_D) {
             DN(16, 1) DN(16, 2) DN(16, 3) DN(16, 4) DN(16, 5) DN(16, 6) DN(16, 7) DN(16, 8)
             default: return hipErrorInvalidValue;
         }
     } else {
+#undef DN
+#define DN(DL, DD)                                                   \
+    case DD:                                                         \
+        if (sh) DNV(DL, DD, true, false); else DNV(DL, DD, false, false); \
+        break;
         switch (p.down_D) {
             DN(64, 1) DN(64, 2) DN(64, 3) DN(64, 4) DN(64, 5) DN(64, 6) DN(64, 7) DN(64, 8)
             default: return hipErrorInvalidValue;
         }
     }
 #undef DN
+#undef DNV
     return hipGetLastError();
 }
 
@@ -443,6 +643,25 @@ static hipError_t launch_expert(const DecodePlan& p, DecodeArgs& a, hipStream_t 
     return launch_down<FMT>(p, a, s);
 }
 
+template <int FMT, int GD, int GP>
+static hipError_t launch_topk_gateup(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
+    dim3 grid(a.k * a.gt_r + a.n_sd), block(256);
+#define TG(DL, DD) case DD: hipLaunchKernelGGL((k_topk_gateup<FMT, GD, GP, DL, DD>), grid, block, 0, s, a); break;
+    if (p.down_L == 16) {
+        switch (p.down_D) {
+            TG(16, 1) TG(16, 2) TG(16, 3) TG(16, 4) TG(16, 5) TG(16, 6) TG(16, 7) TG(16, 8)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.down_D) {
+            TG(64, 1) TG(64, 2) TG(64, 3) TG(64, 4) TG(64, 5) TG(64, 6) TG(64, 7) TG(64, 8)
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef TG
+    return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t launch_layer(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
     const int n1 = (a.E + 3) / 4 + (a.has_shared ? a.gt_s : 0);
@@ -454,13 +673,17 @@ static hipError_t launch_layer(const DecodePlan& p, DecodeArgs& a, hipStream_t s
 #undef RS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-#define TG(GD, GP) case GD: hipLaunchKernelGGL((k_topk_gateup<FMT, GD, GP>), dim3(a.k * a.gt_r), dim3(256), 0, s, a); break;
     switch (p.gate_D) {
-        TG(1, 4) TG(2, 4) TG(3, 4) TG(4, 4) TG(5, 4) TG(6, 2) TG(7, 2) TG(8, 2)
+        case 1: e = launch_topk_gateup<FMT, 1, 4>(p, a, s); break;
+        case 2: e = launch_topk_gateup<FMT, 2, 4>(p, a, s); break;
+        case 3: e = launch_topk_gateup<FMT, 3, 4>(p, a, s); break;
+        case 4: e = launch_topk_gateup<FMT, 4, 4>(p, a, s); break;
+        case 5: e = launch_topk_gateup<FMT, 5, 4>(p, a, s); break;
+        case 6: e = launch_topk_gateup<FMT, 6, 2>(p, a, s); break;
+        case 7: e = launch_topk_gateup<FMT, 7, 2>(p, a, s); break;
+        case 8: e = launch_topk_gateup<FMT, 8, 2>(p, a, s); break;
         default: return hipErrorInvalidValue;
     }
-#undef TG
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_down<FMT>(p, a, s);
 }
@@ -477,6 +700,7 @@ static DecodeArgs make_args(const DecodePlan& p, int fmt, int E, int H, int I, i
     a.h = reinterpret_cast<float*>(base + kCounterBytes);
     a.logits = reinterpret_cast<float*>(base + kCounterBytes + h_bytes);
     a.sel = reinterpret_cast<const void**>(base + kCounterBytes + h_bytes + l_bytes);
+    a.ysh = nullptr;
     a.y = y;
     a.E = E; a.k = k; a.H = H; a.I = I;
     a.has_shared = sh_gate ? 1 : 0;
@@ -507,6 +731,13 @@ hipError_t launch_layer_decode(int fmt, const DecodePlan& p, int E, int H, int I
     a.idx_out = idx_out;
     a.w_out = w_out;
     a.w = w_out;  // the down launch reads the published weights
+    if (a.has_shared) {
+        // the shared expert's down rows move to the top-k launch
+        const size_t sel_bytes = align256((size_t)k * sizeof(void*));
+        a.ysh = reinterpret_cast<float*>(reinterpret_cast<char*>(a.sel) + sel_bytes);
+        a.n_items = k;
+        a.n_sd = (2 * (H / kDownRB) + 3) / 4;
+    }
     return fmt == kFmtNvfp4 ? launch_layer<kFmtNvfp4>(p, a, s) : launch_layer<kFmtMxfp4>(p, a, s);
 }
 

@@ -81,7 +81,7 @@ hipError_t launch_route(int H, int E, int k, int T, const float* x, const float*
                         float* logits_out, void* ws, hipStream_t s) {
     char* base = reinterpret_cast<char*>(ws);
     const int DV = H / 256;
-    if (T <= kRouteTicketMaxT) {
+    if (T <= kRouteSplitMaxT) {
         float* lg = logits_out ? logits_out : reinterpret_cast<float*>(base + kCounterBytes);
         dim3 grid(E, T), block(64);
 #define RS(D) \

@@ -108,51 +108,110 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+// Unsigned max over all 64 lanes (uniform result).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dppu<0xB1>(v));
+    v = max(v, dppu<0x4E>(v));
+    v = max(v, dppu<0x141>(v));
+    v = max(v, dppu<0x140>(v));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key; +0
+// and -0 must be folded before): negative values have all bits flipped,
+// others get the sign bit set. A NaN with the sign bit clear maps above
+// +inf.
+__device__ __forceinline__ uint32_t f32_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 constexpr int kTopkMaxE = 1024;
 
-// Top-k of E <= 64 * NI logits by one full wave: afterwards lane j < k holds
-// the j-th chosen expert (larger logit first, lower expert index first among
-// equal logits) in my_e and its weight, the softmax renormalised over the
-// chosen k, in my_w. LOAD(e) reads logit e (0 <= e < E).
-// Lane l holds experts l*NI .. l*NI + NI - 1, so among lanes holding the
-// round's maximum the lowest lane holds the lowest expert index. All loads
-// are issued before the first use (no load under a branch).
-// Non-finite logits can leave my_e outside [0, E); callers treat such an
-// index as invalid.
+// Top-k of E <= 64 * NI logits by one full wave: afterwards lane j < kk
+// holds the j-th chosen expert (larger logit first, lower expert index first
+// among equal logits) in my_e and its weight, the softmax renormalised over
+// the first kk chosen, in my_w. LOAD(e) reads logit e (0 <= e < E); kk <= E.
+// The logits are compared as order-preserving integer keys (-0 folded onto
+// +0; a NaN ranks above +inf, so every chosen index is in [0, E)).
+// Lane l holds experts l*NI .. l*NI + NI - 1 and first sorts them (key
+// descending, then index ascending; Batcher's odd-even merge network over
+// registers). A round then only compares the lanes' heads: the largest head
+// wins, and among equal heads the lowest lane, which holds the lowest expert
+// indices; the winning lane shifts its sorted list by one. All loads are
+// issued before the first use (no load under a branch).
 template <int NI, class LOAD>
-__device__ __forceinline__ void topk_select_n(LOAD load, int E, int k, int& my_e, float& my_w) {
+__device__ __forceinline__ void topk_select_n(LOAD load, int E, int kk, int& my_e, float& my_w) {
     const int lane = threadIdx.x & 63;
-    const float NEG = -__builtin_inff();
-    float v[NI];
+    uint32_t v[NI];
+    int ix[NI];
+    {
+        float f[NI];
 #pragma unroll
-    for (int i = 0; i < NI; i++) v[i] = load(min(lane * NI + i, E - 1));
+        for (int i = 0; i < NI; i++) f[i] = load(min(lane * NI + i, E - 1));
 #pragma unroll
-    for (int i = 0; i < NI; i++) v[i] = lane * NI + i < E ? v[i] + 0.0f : NEG;  // + 0 folds -0 onto +0
-    my_e = -1;
-    float my_l = 0.f;
-    for (int j = 0; j < k; j++) {
-        float m = v[0];
-#pragma unroll
-        for (int i = 1; i < NI; i++) m = fmaxf(m, v[i]);
-        m = wave_max(m);
-        int f = NI;  // first local slot holding the maximum
-#pragma unroll
-        for (int i = NI - 1; i >= 0; i--) f = v[i] == m ? i : f;
-        const unsigned long long b = __ballot(f < NI);
-        const int L = b ? __ffsll((long long)b) - 1 : 0;
-        const int fl = __builtin_amdgcn_readlane(f, L);
-        const int e = b ? L * NI + fl : -1;
-#pragma unroll
-        for (int i = 0; i < NI; i++) v[i] = (lane == L && i == fl) ? NEG : v[i];
-        if (lane == j) {
-            my_e = e;
-            my_l = m;
+        for (int i = 0; i < NI; i++) {
+            v[i] = lane * NI + i < E ? f32_key(f[i] + 0.0f) : 0u;  // + 0 folds -0 onto +0; 0 = padding
+            ix[i] = i;
         }
     }
+    // local sort: position a before b iff v[a] > v[b], or equal and ix[a] < ix[b]
+#pragma unroll
+    for (int p = 1; p < NI; p <<= 1) {
+#pragma unroll
+        for (int q = p; q >= 1; q >>= 1) {
+#pragma unroll
+            for (int j = q % p; j + q < NI; j += 2 * q) {
+#pragma unroll
+                for (int i = 0; i < q && i + j + q < NI; i++) {
+                    const int lo = i + j, hi = i + j + q;
+                    if (lo / (2 * p) == hi / (2 * p)) {
+                        const bool keep = v[lo] > v[hi] || (v[lo] == v[hi] && ix[lo] < ix[hi]);
+                        const uint32_t va = v[lo], vb = v[hi];
+                        const int ia = ix[lo], ib = ix[hi];
+                        v[lo] = keep ? va : vb;
+                        v[hi] = keep ? vb : va;
+                        ix[lo] = keep ? ia : ib;
+                        ix[hi] = keep ? ib : ia;
+                    }
+                }
+            }
+        }
+    }
+    my_e = -1;
+    uint32_t my_k = 0;
+    for (int j = 0; j < kk; j++) {
+        const uint32_t m = wave_max_u32(v[0]);
+        const unsigned long long b = __ballot(v[0] == m);  // never empty: m is some lane's head
+        const int L = __ffsll((long long)b) - 1;
+        const int e = L * NI + __builtin_amdgcn_readlane(ix[0], L);
+        if (lane == L) {
+#pragma unroll
+            for (int i = 0; i + 1 < NI; i++) {
+                v[i] = v[i + 1];
+                ix[i] = ix[i + 1];
+            }
+            v[NI - 1] = 0u;
+        }
+        if (lane == j) {
+            my_e = e;
+            my_k = m;
+        }
+    }
+    const float my_l = key_f32(my_k);
     const float lmax = __shfl(my_l, 0, 64);
-    const float ex = lane < k ? expf(my_l - lmax) : 0.f;
+    const float ex = lane < kk ? expf(my_l - lmax) : 0.f;
     const float z = wave_sum(ex);
     my_w = ex / z;
 }
@@ -199,9 +258,13 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
+// p and bytes must be wave-uniform; they are read from the first active lane.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(p)), (short)0, (int)bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(p)), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+// The wave's index in its workgroup, as a value the compiler knows is uniform.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ uint32_t ld_b32(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }

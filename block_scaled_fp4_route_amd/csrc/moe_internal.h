@@ -9,18 +9,12 @@
 
 namespace moe {
 
-// Workspace: [0, kCounterBytes) completion counters (zero between calls),
-// then the data regions of each mode.
+// Workspace: [0, kCounterBytes) is reserved (no kernel writes it, so it
+// stays as the caller zero-filled it), then the data regions of each mode.
 constexpr size_t kCounterBytes = 4096;
-constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
-constexpr int kRouteTicketMaxT = 16;  // tokens routed by the split-row kernel
-// completion counters inside the counter region (int offsets)
-constexpr int kCntReady = 0;       // decode: gate/up tiles finished, per slot (<= 33)
-constexpr int kCntConsumed = 64;   // decode: down workgroups that read h, per slot
-constexpr int kCntDone = 128;      // decode: partial rows finished, per row block (<= 768)
-constexpr int kCntRoute = 1000;    // router: logit rows finished, per token (<= 16)
+constexpr int kRouteSplitMaxT = 16;  // tokens routed by the row-split kernels
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 

@@ -32,9 +32,10 @@
  *    MOE_ERR_UNSUPPORTED; there is no slow or silent fallback.
  *  - Faults inside kernels surface at the caller's next synchronisation.
  *  - Workspace `ws`: device memory of at least moe_workspace_bytes() bytes,
- *    256-byte aligned, ZERO-FILLED ONCE before its first use. Its first 4096
- *    bytes hold completion counters that every call leaves at zero again.
- *    Calls that share one workspace must not run concurrently.
+ *    256-byte aligned. Its contents on entry do not matter and nothing in it
+ *    carries over from one call to the next (its first 4096 bytes are
+ *    reserved and never written). Calls that share one workspace must not
+ *    run concurrently.
  *  - The library keeps no mutable global state and is reentrant.
  */
 #ifndef MOE_FP4_H

@@ -146,6 +146,8 @@ def test_decode_deterministic_reruns(m, orc):
     ("nvfp4", 4096, 4096, 2, 2),   # largest supported H and I
     ("mxfp4", 4096, 4096, 2, 1),
     ("nvfp4", 3072, 1040, 6, 3),   # down rows of 130 dwords: ragged lane coverage
+    ("nvfp4", 512, 256, 40, 32),   # k = 32: sixteen routed pairs fill the down workgroup
+    ("mxfp4", 512, 320, 9, 7),     # odd k: the last down pair holds one item
 ])
 def test_decode_edge_shapes(m, orc, fmt, H, I, E, k):
     wl = sg.Workload("edge", 90, H, I, E, k, fmt, 1, 1, False, "router", 0.0,
@@ -211,8 +213,8 @@ def test_route_exact_logits_with_ties(m, orc, T):
 
 
 def test_one_workspace_across_layers_and_calls(m, orc):
-    """Route and decode of several layers share one workspace (its counters
-    must be back at zero after every call); each layer matches the oracle."""
+    """Route and decode of several layers share one workspace (its reserved
+    first 4096 bytes are never written); each layer matches the oracle."""
     wl = sg.get("qwen_decode")
     E = 48
     d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
@@ -230,7 +232,7 @@ def test_one_workspace_across_layers_and_calls(m, orc):
             m.moe_route(d, x, 1, Wr, idx, w, None, ws)
             m.moe_expert_decode(d, x, m.expert_ptr_table(blocks), idx, w, shared, y, ws)
         torch.cuda.synchronize()
-        assert not ws[:4096].any(), "completion counters not reset"
+        assert not ws[:4096].any(), "reserved workspace bytes written"
         _, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
         assert (idx.cpu().numpy() == oi[0]).all()
         hb = host_blocks(blocks, oi[0])
@@ -296,7 +298,7 @@ def test_layer_decode_parity_and_equal_to_two_calls(m, orc, name, E, with_shared
     assert torch.equal(idx, idx2)
     assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
-    assert not ws[:4096].any(), "completion counters not reset"
+    assert not ws[:4096].any(), "reserved workspace bytes written"
 
     _, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
     gi = idx.cpu().numpy()
@@ -314,7 +316,7 @@ def test_layer_decode_parity_and_equal_to_two_calls(m, orc, name, E, with_shared
 def test_layer_decode_many_layers_one_workspace(m, orc):
     """Several layers enqueued back to back on one workspace with no host
     synchronisation between them (each with its own seeded input); every
-    layer then matches the oracle and the counters are back at zero."""
+    layer then matches the oracle and the reserved bytes stay untouched."""
     wl = sg.get("qwen_decode")
     E = 96
     d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
@@ -364,4 +366,56 @@ def test_layer_decode_exact_router_ties(m, orc):
     assert (idx.cpu().numpy() == oi[0]).all()
     hb = host_blocks(blocks, oi[0])
     ref, _ = orc.moe_decode("nvfp4", H, I, x.numpy(), [hb[int(e)] for e in oi[0]], ow[0], nthreads=NTHREADS)
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
+
+
+def test_workspace_contents_do_not_matter(m):
+    """The workspace needs no initialisation: a workspace full of junk gives
+    bit-identical results to a zero-filled one (both entry points)."""
+    wl = sg.get("qwen_decode")
+    E = 64
+    blocks, Wr, shared, x = _layer_inputs(wl, E, 1, 6, True)
+    d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
+    ptrs = m.expert_ptr_table(blocks)
+    outs = []
+    for fill in (0x00, 0xFF, 0x7F):
+        ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+        ws.fill_(fill)
+        y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+        y2 = torch.empty_like(y)
+        idx = torch.empty(wl.k, dtype=torch.int32, device="cuda")
+        w = torch.empty(wl.k, dtype=torch.float32, device="cuda")
+        m.moe_layer_decode(d, x, Wr, ptrs, shared, y, idx, w, ws)
+        ws.fill_(fill)
+        m.moe_expert_decode(d, x, ptrs, idx, w, shared, y2, ws)
+        torch.cuda.synchronize()
+        outs.append((y.view(torch.int32).clone(), y2.view(torch.int32).clone(), idx.clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(p, q) for p, q in zip(o, outs[0]))
+    assert torch.equal(outs[0][0], outs[0][1])
+
+
+@pytest.mark.parametrize("k", [31, 32])
+def test_layer_decode_large_k_with_shared(m, orc, k):
+    """k routed experts plus the shared expert: more down units than one
+    workgroup's waves, so the down launch loops waves over single items."""
+    wl = sg.Workload("largek", 92, 1024, 256, 48, k, "nvfp4", 1, 1, True, "router", 0.0, 0x18, 0x48, False)
+    blocks, Wr, shared, x = _layer_inputs(wl, wl.E, 0, 0, True)
+    d = m.desc(wl.H, wl.I, wl.E, k, wl.fmt)
+    ptrs = m.expert_ptr_table(blocks)
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y)
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    w = torch.empty(k, dtype=torch.float32, device="cuda")
+    m.moe_layer_decode(d, x, Wr, ptrs, shared, y, idx, w, ws)
+    m.moe_expert_decode(d, x, ptrs, idx, w, shared, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    _, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), k)
+    gi = idx.cpu().numpy()
+    assert (gi == oi[0]).all()
+    hb = host_blocks(blocks, gi)
+    ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x.cpu().numpy(), [hb[int(e)] for e in gi], ow[0],
+                            shared=[bf16_bits(s) for s in shared], nthreads=NTHREADS)
     assert rel_err(y.cpu().numpy(), ref) <= TOL
