@@ -33,8 +33,9 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 
 # HBM bytes per call of the roofline's kernels from rocprofv3 --pmc
 # (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain 1 GiB copy gives),
-# per workload; None until counters were taken on the current kernels.
-TRAFFIC: dict = {}
+# per workload; absent until counters were taken on the current kernels.
+# qwen_decode: k_gateup<1,5,4> + k_down_combine<1,16,5,true,true>.
+TRAFFIC: dict = {"qwen_decode": 38345216}
 
 
 def log(*a):
