@@ -112,21 +112,21 @@ struct XStage {
 // ----------------------------------------------------------------------------
 // gate/up rows + SiLU*mul for one tile of a routed expert (block `blk`, NULL
 // for an invalid index) or of the shared expert, into slot `slot` of h.
-// Wave v handles row pairs pair0 .. pair0+P-1 (gate row i and up row i).
-// Lane l reads code dwords l + 64m (m < D) of every row: 8 codes at columns
-// 8(l+64m)..+7 whose activations it keeps in registers. Gate and up codes
-// ([I][H/2] each) are adjacent in the block, as are their scales; the bf16
-// shared expert uses the same lane/column map with 16-byte chunks.
-// xst holds this thread's part of x, already requested; every thread of the
-// workgroup calls this (it contains a barrier).
+// Wave v handles row pairs pair0 .. pair0+P-1: lanes 0-31 the gate row,
+// lanes 32-63 the up row of each pair. Lane s (= lane mod 32) reads 16-code
+// chunks c = s + 32m (m < D) of its row: 8 bytes of codes (one NVFP4 scale
+// group) with one scale byte, or 32 bytes of bf16 for the shared expert.
+// The activations of chunk c come from LDS when the chunk is used, once for
+// all P pairs. Gate and up codes ([I][H/2] each) are adjacent in the block,
+// as are their scales. xst holds this thread's part of x, already
+// requested; every thread of the workgroup calls this (it has a barrier).
 template <int FMT, int D, int P, bool SHARED>
 __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const void* blk, int pair0, f4v* xs,
                                             const XStage<512 * D>& xst) {
     constexpr int K = 512 * D;     // H
-    constexpr int KD = K / 8;      // code dwords per row (= 16-byte bf16 chunks per shared row)
     constexpr int G = Fmt<FMT>::G;
     constexpr int KS = K / G;      // scale bytes per row
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, s = lane & 31, half = lane >> 5;  // half 0: gate, 1: up
     const int I = a.I;
     const int np = min(P, I - pair0);  // wave-uniform; <= 0 for idle waves of the last tile
     // an invalid expert index poisons this slot instead of reading anything
@@ -137,69 +137,82 @@ __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const
     // and their sums dropped; an invalid index gets a buffer of 0 bytes, whose
     // loads return 0 without touching memory), so that the compiler's memory
     // counter waits stay exact
-    uint32_t wv[2 * P][D], sv[2 * P][D];
-    uint4 v[2 * P][D];
+    uint2 wv[P][D];
+    uint32_t sv[P][D];
+    uint4 v[P][D][2];
     if (SHARED) {
-        const uint4* gq = reinterpret_cast<const uint4*>(a.sh_gate);
-        const uint4* uq = reinterpret_cast<const uint4*>(a.sh_up);
+        const uint4* q = reinterpret_cast<const uint4*>(half ? a.sh_up : a.sh_gate);
 #pragma unroll
-        for (int r = 0; r < 2 * P; r++) {
-            const size_t row = (size_t)min(pair0 + r % P, I - 1);
+        for (int p = 0; p < P; p++) {
+            const size_t row = (size_t)min(pair0 + p, I - 1);
 #pragma unroll
-            for (int m = 0; m < D; m++) v[r][m] = (r < P ? gq : uq)[row * KD + lane + 64 * m];
+            for (int m = 0; m < D; m++) {
+                const size_t c = s + 32 * m;
+                v[p][m][0] = q[row * (K / 8) + 2 * c];
+                v[p][m][1] = q[row * (K / 8) + 2 * c + 1];
+            }
         }
     } else {
         const rsrc_t rb = make_rsrc(bad ? (const void*)a.x : blk, bad ? 0u : a.block_bytes);
         const uint32_t scl = (uint32_t)3 * I * (K / 2);
 #pragma unroll
-        for (int r = 0; r < 2 * P; r++) {
-            const uint32_t row = (uint32_t)(r / P) * I + min(pair0 + r % P, I - 1);
+        for (int p = 0; p < P; p++) {
+            const uint32_t row = (uint32_t)half * I + min(pair0 + p, I - 1);
 #pragma unroll
             for (int m = 0; m < D; m++) {
-                const uint32_t c = lane + 64 * m;
-                wv[r][m] = ld_b32(rb, row * (K / 2) + 4 * c);
-                sv[r][m] = ld_b8(rb, scl + row * KS + c * 8 / G);
+                const uint32_t c = s + 32 * m;
+                wv[p][m] = ld_b64(rb, row * (K / 2) + 8 * c);
+                sv[p][m] = ld_b8(rb, scl + row * KS + c * 16 / G);
             }
         }
     }
 
-    // 2. x into LDS (it was requested before the weights), then registers:
-    // lane keeps columns 8(lane+64m)..+7
+    // 2. x into LDS (it was requested before the weights)
     xst.store(xs);
     __syncthreads();
     if (np > 0) {
-        float xr[8 * D];
+        // 3. dot products per chunk (its 16 activations read once for all pairs)
+        float acc[P];
+#pragma unroll
+        for (int p = 0; p < P; p++) acc[p] = 0.f;
 #pragma unroll
         for (int m = 0; m < D; m++) {
-            const f4v p0 = xs[2 * (lane + 64 * m)], p1 = xs[2 * (lane + 64 * m) + 1];
-            xr[8 * m + 0] = p0.x; xr[8 * m + 1] = p0.y; xr[8 * m + 2] = p0.z; xr[8 * m + 3] = p0.w;
-            xr[8 * m + 4] = p1.x; xr[8 * m + 5] = p1.y; xr[8 * m + 6] = p1.z; xr[8 * m + 7] = p1.w;
-        }
-        // 3. dot products, row sums, SiLU*mul
-        float acc[2 * P];
+            const int c = s + 32 * m;
+            float xx[16];
 #pragma unroll
-        for (int r = 0; r < 2 * P; r++) {
-            float s = 0.f;
-            if (SHARED) {
-#pragma unroll
-                for (int m = 0; m < D; m++) {
-                    const float* xx = &xr[8 * m];
-                    s = fmaf(bf16_lo(v[r][m].x), xx[0], s); s = fmaf(bf16_hi(v[r][m].x), xx[1], s);
-                    s = fmaf(bf16_lo(v[r][m].y), xx[2], s); s = fmaf(bf16_hi(v[r][m].y), xx[3], s);
-                    s = fmaf(bf16_lo(v[r][m].z), xx[4], s); s = fmaf(bf16_hi(v[r][m].z), xx[5], s);
-                    s = fmaf(bf16_lo(v[r][m].w), xx[6], s); s = fmaf(bf16_hi(v[r][m].w), xx[7], s);
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < D; m++)
-                    s = fmaf(scale_to_f32<FMT>(sv[r][m]), dot8_fp4(wv[r][m], &xr[8 * m]), s);
+            for (int j = 0; j < 4; j++) {
+                const f4v t = xs[4 * c + j];
+                xx[4 * j + 0] = t.x; xx[4 * j + 1] = t.y; xx[4 * j + 2] = t.z; xx[4 * j + 3] = t.w;
             }
-            acc[r] = bad ? __uint_as_float(0x7FC00000u) : wave_sum(s);
-        }
-        if (lane == 0) {
 #pragma unroll
-            for (int p = 0; p < P; p++)
-                if (p < np) a.h[(size_t)slot * I + pair0 + p] = silu_mul(acc[p], acc[P + p]);
+            for (int p = 0; p < P; p++) {
+                if (SHARED) {
+                    float t = acc[p];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; h2++) {
+                        const uint4 u = v[p][m][h2];
+                        const float* x8 = &xx[8 * h2];
+                        t = fmaf(bf16_lo(u.x), x8[0], t); t = fmaf(bf16_hi(u.x), x8[1], t);
+                        t = fmaf(bf16_lo(u.y), x8[2], t); t = fmaf(bf16_hi(u.y), x8[3], t);
+                        t = fmaf(bf16_lo(u.z), x8[4], t); t = fmaf(bf16_hi(u.z), x8[5], t);
+                        t = fmaf(bf16_lo(u.w), x8[6], t); t = fmaf(bf16_hi(u.w), x8[7], t);
+                    }
+                    acc[p] = t;
+                } else {
+                    acc[p] = fmaf(scale_to_f32<FMT>(sv[p][m]), dot16_fp4(wv[p][m].x, wv[p][m].y, xx), acc[p]);
+                }
+            }
+        }
+        // 4. row sums (both rows of a pair in one reduction), SiLU*mul
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            const float r = row16_sum(acc[p]);
+            const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0)) +
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
+            const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32)) +
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
+            if (lane == 0 && p < np)
+                a.h[(size_t)slot * I + pair0 + p] = bad ? __uint_as_float(0x7FC00000u) : silu_mul(g, u);
         }
     }
 }

@@ -66,6 +66,30 @@ __device__ __forceinline__ float dot8_fp4(uint32_t w, const float* x) {
     return a;
 }
 
+// sum_{i<16} e2m1(code i) * x[i] over the 16 codes of (w0, w1) (w0 first,
+// low nibble first), one fma chain.
+__device__ __forceinline__ float dot16_fp4(uint32_t w0, uint32_t w1, const float* x) {
+    f2v p0 = fp4x2<0>(w0), p1 = fp4x2<1>(w0), p2 = fp4x2<2>(w0), p3 = fp4x2<3>(w0);
+    f2v p4 = fp4x2<0>(w1), p5 = fp4x2<1>(w1), p6 = fp4x2<2>(w1), p7 = fp4x2<3>(w1);
+    float a = p0.x * x[0];
+    a = fmaf(p0.y, x[1], a);
+    a = fmaf(p1.x, x[2], a);
+    a = fmaf(p1.y, x[3], a);
+    a = fmaf(p2.x, x[4], a);
+    a = fmaf(p2.y, x[5], a);
+    a = fmaf(p3.x, x[6], a);
+    a = fmaf(p3.y, x[7], a);
+    a = fmaf(p4.x, x[8], a);
+    a = fmaf(p4.y, x[9], a);
+    a = fmaf(p5.x, x[10], a);
+    a = fmaf(p5.y, x[11], a);
+    a = fmaf(p6.x, x[12], a);
+    a = fmaf(p6.y, x[13], a);
+    a = fmaf(p7.x, x[14], a);
+    a = fmaf(p7.y, x[15], a);
+    return a;
+}
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -267,6 +291,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ uint32_t ld_b32(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint2 ld_b64(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
 }
 __device__ __forceinline__ uint32_t ld_b8(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
