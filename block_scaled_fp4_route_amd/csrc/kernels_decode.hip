@@ -167,9 +167,10 @@ __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const
         }
     }
 
-    // 2. x into LDS (it was requested before the weights)
+    // 2. x into LDS (it was requested before the weights); the barrier orders
+    // LDS only, so the weight loads stay in flight across it
     xst.store(xs);
-    __syncthreads();
+    lds_barrier();
     if (np > 0) {
         // 3. dot products per chunk (its 16 activations read once for all pairs)
         float acc[P];
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(256) void k_gateup(DecodeArgs a) {
         const void* t[kTableRegs];
         load_table(a, t);
         store_table(a, t, tbl);
-        __syncthreads();
+        lds_barrier();
         if (bid == 0 && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, ej);
         gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, e), ((bid % a.gt_r) * 4 + v) * GP, buf, xst);
     } else {
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(256) void k_topk_gateup(DecodeArgs a) {
         }
     }
     store_table(a, t, tbl);
-    __syncthreads();
+    lds_barrier();
     if (publisher && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, e);
     gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, sel_e),
                                     ((bid % a.gt_r) * 4 + wave_id()) * GP, buf, xst);

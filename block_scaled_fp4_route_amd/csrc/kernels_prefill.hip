@@ -79,6 +79,13 @@ static PrefillWs prefill_layout(int fmt, int H, int I, int E, int k, int T, void
     return w;
 }
 
+// The grouped GEMMs address their activation operands with 32-bit buffer
+// offsets and use offsets from 0x7FFFFFF0 up as "no load".
+bool prefill_tokens_supported(int H, int I, int k, int T) {
+    const size_t lim = 0x7FFFFFF0u;
+    return (size_t)T * H * 2 < lim && (size_t)T * k * I * 2 < lim && (size_t)T * H * 4 < ((size_t)1 << 32);
+}
+
 bool prefill_supported(int fmt, int H, int I, int E, int k) {
     if (E < 1 || E > kMaxE || k < 1 || k > kMaxK) return false;
     if (fmt == kFmtNvfp4) return H % 256 == 0 && I % 128 == 0 && H <= 16384 && I <= 16384;
@@ -282,20 +289,17 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
 // order-independent). The codes are decoded to bf16 exactly (e2m1 x E4M3 has
 // at most 6 significant bits).
 // Workgroup -> (M-tile, N-tile). Workgroups are dispatched round-robin over
-// the 8 XCDs (each with its own L2), so workgroup b runs on XCD b % 8. The
-// R = ntiles * NT real tiles are cut into 8 contiguous ranges, one per XCD,
-// in (M-tile, N-tile) order: the N-tiles of one M-tile (same gathered rows)
-// and the consecutive M-tiles of one expert (same weights) then share an L2.
+// the 8 XCDs (each with its own L2), so workgroup b runs on XCD b % 8. M-tile
+// t goes to XCD t % 8 and all NT N-tiles of an M-tile (the same gathered
+// activation rows) to that XCD, one after the other: the tile list is sorted
+// heaviest expert first, so dealing M-tiles round-robin spreads the full
+// tiles evenly over the XCDs. The grid is 8 * ceil(max_tiles / 8) * NT.
 // Returns false for workgroups beyond the real tiles.
 __device__ __forceinline__ bool map_tile(int ntiles, int NT, int& tile, int& nt) {
-    const int R = ntiles * NT;
-    const int per = (R + 7) / 8;
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
-    const int L = x * per + j;
-    if (j >= per || L >= R) return false;
-    tile = L / NT;
-    nt = L % NT;
-    return true;
+    tile = x + 8 * (j / NT);
+    nt = j % NT;
+    return tile < ntiles;
 }
 
 struct GemmArgs {
@@ -312,7 +316,22 @@ struct GemmArgs {
     float* h_pre;           // optional debug
     float* h_q;             // optional debug (NVFP4)
     int E, H, I, k, NT;     // NT = N-tiles per M-tile
+    uint32_t a_bytes;       // bytes of a_src
+    uint32_t block_bytes;   // bytes of one expert block
 };
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (loads complete in issue order) and this wave's LDS accesses are done, then
+// a workgroup barrier. The direct-to-LDS loads have no register result, so
+// the compiler cannot place this wait itself, and a fenced barrier would
+// drain every outstanding load (the compiler must assume any of them writes
+// LDS). The memory clobber keeps the compiler from moving memory accesses
+// across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // Decode 8 e2m1 codes (dword d) times scale s to 8 bf16 (exact).
 __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
@@ -325,99 +344,130 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 }
 
 // Shared K loop of the two NVFP4 GEMMs: acc[rb][cb] += A[64 rows] x B[4
-// column blocks]^T over K (= KTOT) in chunks of BK (128 or 256). a_row(r)
-// gives the element offset of A row r (or -1 for a padding row); brow[cb] is
-// the weight row of this lane's column in block cb; codes/scales are the
-// weight matrix regions with KTOT/2 code bytes and KTOT/16 scale bytes per
-// row. Within a chunk, lane group g = lane/16 owns K = g*BK/4 .. +BK/4 (one
-// or two 16-byte code loads per column block, 2 or 4 scale bytes) and MFMA
-// step s consumes its elements 8s..8s+7; the A tile in LDS is read with the
-// same K mapping. The next chunk's loads are in flight during the current
-// chunk's MFMAs.
+// column blocks]^T over K (= KTOT) in chunks of BK (128 or 256). A is a
+// buffer of a_bytes bytes; a_row(r) gives the element offset of A row r
+// (0 <= r < rows). blk is the expert block (block_bytes), codes_off and
+// scl_off the byte offsets of the weight matrix's code and scale regions
+// (KTOT/2 code bytes and KTOT/16 scale bytes per row), brow[cb] the weight
+// row of this lane's column in block cb. Within a chunk, lane group g =
+// lane/16 owns K = g*BK/4 .. +BK/4 (one or two 16-byte code loads per column
+// block, 2 or 4 scale bytes) and MFMA step s consumes its elements 8s..8s+7;
+// the A tile in LDS is read with the same K mapping.
+// Pipeline: the A tile of chunk ch+1 goes from memory straight into LDS
+// (buffer_load ... lds, no registers) while chunk ch is computed, and the
+// weight fragments run two chunks ahead in two register sets (steps go in
+// pairs so that the sets have fixed registers). Every step issues the same
+// loads; those past the last chunk use an out-of-range offset, which returns
+// zeros without touching memory. The compiler can then count outstanding
+// loads exactly, and the explicit waits before each barrier cover the LDS
+// loads it cannot see. A rows are stored without padding, 16-byte piece p of
+// row r at slot r*SPR + (p ^ (r & 7)), which keeps the fragment reads of 8
+// consecutive rows on distinct bank groups. Rows past `rows` load row 0
+// (their sums are never stored).
+constexpr uint32_t kOOB = 0x7FFFFFF0u;  // beyond every buffer here: loads return 0
+
 template <int BK, class AROW>
-__device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, AROW a_row, int rows,
-                                         const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scl,
-                                         const int (&brow)[4], int KTOT, __bf16* lds) {
-    constexpr int LD = BK + 8;        // LDS row stride (bf16), padded
-    constexpr int QK = BK / 4;        // K per lane group (and per A-loader thread)
+__device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, uint32_t a_bytes,
+                                         AROW a_row, int rows, const void* blk, uint32_t block_bytes,
+                                         uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
+                                         __bf16* lds) {
+    constexpr int SPR = BK / 8;       // 16-byte pieces per A row
+    constexpr int NAI = SPR / 4;      // A loads per wave per chunk (64 rows x SPR pieces over 256 lanes)
+    constexpr int QK = BK / 4;        // K per lane group
     constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
     constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
-    const int tid = threadIdx.x, lane = tid & 63;
+    constexpr int NBL = 4 * (NB + 1); // weight loads per lane per chunk (codes + scales)
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, m16 = lane & 15;
-    // A loader: 16-byte piece c = tid % CPR of rows tid / CPR + i * RPI: the
-    // lanes of one row read its BK*2 bytes contiguously, and in LDS 8
-    // consecutive lanes write 8 consecutive 16-byte slots (no bank conflicts
-    // with the odd 16-byte row stride).
-    constexpr int CPR = BK / 8;             // 16-byte pieces per row (16 or 32)
-    constexpr int RPI = 256 / CPR;          // rows per loader instruction (16 or 8)
-    constexpr int NA = 64 / RPI;            // loader instructions per chunk (4 or 8)
-    const int lc = tid % CPR, lr0 = tid / CPR;
-    int arow[NA];
+    const rsrc_t ra = make_rsrc(A, a_bytes);
+    const rsrc_t rb = make_rsrc(blk, block_bytes);
+    // this lane's A loads: LDS slot P = (wave*NAI + i)*64 + lane
+    uint32_t aoff[NAI];
 #pragma unroll
-    for (int i = 0; i < NA; i++) arow[i] = a_row(lr0 + i * RPI);
+    for (int i = 0; i < NAI; i++) {
+        const int P = (wave * NAI + i) * 64 + lane, r = P / SPR, q = P % SPR;
+        aoff[i] = 2u * (uint32_t)(a_row(r < rows ? r : 0) + 8 * (q ^ (r & 7)));
+    }
+    uint32_t boff[4], soff[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) {
+        boff[cb] = codes_off + (uint32_t)brow[cb] * (KTOT / 2) + (QK / 2) * g;
+        soff[cb] = scl_off + (uint32_t)brow[cb] * (KTOT / 16) + (QK / 16) * g;
+    }
     const int nchunks = KTOT / BK;
-    uint4 anext[NA];
-    uint4 bnext[4][NB];
-    uint32_t snext[4];
-    auto load_chunk = [&](int ch) {
-        const int k0 = ch * BK;
+    auto issue_a = [&](int ch, int buf) {
+        const bool on = ch < nchunks;
 #pragma unroll
-        for (int i = 0; i < NA; i++)
-            anext[i] = arow[i] >= 0 ? *reinterpret_cast<const uint4*>(A + (size_t)arow[i] + k0 + 8 * lc)
-                                    : uint4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < NAI; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(lds + (size_t)buf * 64 * BK + (size_t)(wave * NAI + i) * 64 * 8),
+                16, on ? aoff[i] + 2u * ch * BK : kOOB, 0, 0, 0);
+    };
+    auto load_b = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4]) {
+        const bool on = ch < nchunks;
 #pragma unroll
         for (int cb = 0; cb < 4; cb++) {
-            const size_t r = (size_t)brow[cb];
-            const uint4* src = reinterpret_cast<const uint4*>(codes + r * (KTOT / 2) + k0 / 2 + (QK / 2) * g);
 #pragma unroll
-            for (int i = 0; i < NB; i++) bnext[cb][i] = src[i];
-            const uint8_t* sp = scl + r * (KTOT / 16) + k0 / 16 + (QK / 16) * g;
-            snext[cb] = NB == 1 ? (uint32_t) * reinterpret_cast<const uint16_t*>(sp)
-                                : *reinterpret_cast<const uint32_t*>(sp);
+            for (int i = 0; i < NB; i++) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, on ? boff[cb] + ch * (BK / 2) + 16 * i : kOOB, 0, 0);
+                bw[cb][i] = uint4{v[0], v[1], v[2], v[3]};
+            }
+            const uint32_t so = on ? soff[cb] + ch * (BK / 16) : kOOB;
+            bs[cb] = NB == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b32(rb, so, 0, 0);
         }
     };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NA; i++)
-            *reinterpret_cast<uint4*>(lds + (size_t)buf * 64 * LD + (lr0 + i * RPI) * LD + 8 * lc) = anext[i];
-    };
-    load_chunk(0);
-    store_a(0);
-    __syncthreads();
-    for (int ch = 0; ch < nchunks; ch++) {
-        const int cur = ch & 1;
+    uint4 b0[4][NB], b1[4][NB];
+    uint32_t s0[4], s1[4];
+    issue_a(0, 0);
+    load_b(0, b0, s0);
+    load_b(1, b1, s1);
+    vm_wait_barrier<NBL>();  // A(0) (and B(0)) landed
+    // one chunk: take its weights out of set (bw, bs), refill the set with
+    // chunk ch+2, load A(ch+1) into the other LDS buffer, compute, then wait
+    // for A(ch+1): the barrier also ends every wave's reads of this chunk's
+    // buffer, which A(ch+2) overwrites
+    auto step = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4]) {
         uint4 bc[4][NB];
         uint32_t sc[4];
 #pragma unroll
         for (int cb = 0; cb < 4; cb++) {
 #pragma unroll
-            for (int i = 0; i < NB; i++) bc[cb][i] = bnext[cb][i];
-            sc[cb] = snext[cb];
+            for (int i = 0; i < NB; i++) bc[cb][i] = bw[cb][i];
+            sc[cb] = bs[cb];
         }
-        if (ch + 1 < nchunks) load_chunk(ch + 1);
-        const __bf16* At = lds + (size_t)cur * 64 * LD;
+        issue_a(ch + 1, (ch + 1) & 1);
+        load_b(ch + 2, bw, bs);
+        if (ch < nchunks) {
+            const __bf16* At = lds + (size_t)(ch & 1) * 64 * BK;
 #pragma unroll
-        for (int s = 0; s < NS; s++) {
-            bf16x8 bf[4];
+            for (int s = 0; s < NS; s++) {
+                bf16x8 bf[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; cb++) {
-                const uint4 q = bc[cb][s / 4];
-                const uint32_t d = (s & 3) == 0 ? q.x : ((s & 3) == 1 ? q.y : ((s & 3) == 2 ? q.z : q.w));
-                const float sv = e4m3_to_f32((sc[cb] >> (8 * (s / 2))) & 0xFFu);
-                bf[cb] = dequant8_bf16(d, sv);
-            }
+                for (int cb = 0; cb < 4; cb++) {
+                    const uint4 q = bc[cb][s / 4];
+                    const uint32_t d = (s & 3) == 0 ? q.x : ((s & 3) == 1 ? q.y : ((s & 3) == 2 ? q.z : q.w));
+                    const float sv = e4m3_to_f32((sc[cb] >> (8 * (s / 2))) & 0xFFu);
+                    bf[cb] = dequant8_bf16(d, sv);
+                }
+                const int p = (QK / 8) * g + s;  // 16-byte piece of the fragment
 #pragma unroll
-            for (int rb = 0; rb < 4; rb++) {
-                if (16 * rb < rows) {  // uniform: skip padding row blocks of a short tile
-                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(At + (16 * rb + m16) * LD + QK * g + 8 * s);
+                for (int rb = 0; rb < 4; rb++) {
+                    if (16 * rb < rows) {  // uniform: skip padding row blocks of a short tile
+                        const int r = 16 * rb + m16;
+                        const bf16x8 af = *reinterpret_cast<const bf16x8*>(At + (r * SPR + (p ^ (r & 7))) * 8);
 #pragma unroll
-                    for (int cb = 0; cb < 4; cb++)
-                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[cb], acc[rb][cb], 0, 0, 0);
+                        for (int cb = 0; cb < 4; cb++)
+                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[cb], acc[rb][cb], 0, 0, 0);
+                    }
                 }
             }
         }
-        if (ch + 1 < nchunks) store_a(cur ^ 1);
-        __syncthreads();
+        vm_wait_barrier<NBL>();
+    };
+    for (int ch = 0; ch < nchunks; ch += 2) {
+        step(ch, b0, s0);
+        step(ch + 1, b1, s1);
     }
 }
 
@@ -425,7 +475,7 @@ constexpr int kBKGate = 256;  // K chunk of the gate/up GEMM (K = H)
 constexpr int kBKDown = 128;  // K chunk of the down GEMM (K = I)
 
 __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * (kBKGate + 8)];
+    __shared__ __bf16 lds[2 * 64 * kBKGate];
     int tile, nt;
     if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
@@ -434,21 +484,21 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int c0 = nt * 128 + 32 * wave;
-    const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
-    const uint8_t* codes = blk;                               // gate rows then up rows, H/2 bytes each
-    const uint8_t* scl = blk + (size_t)3 * I * H / 2;         // gate scales then up scales, H/16 each
+    const void* blk = a.expert_ptrs[e];
+    const uint32_t codes_off = 0;                             // gate rows then up rows, H/2 bytes each
+    const uint32_t scl_off = (uint32_t)3 * I * H / 2;         // gate scales then up scales, H/16 each
     const int m16 = lane & 15;
     const int brow[4] = {c0 + m16, c0 + 16 + m16, I + c0 + m16, I + c0 + 16 + m16};
     const __bf16* X = reinterpret_cast<const __bf16*>(a.a_src);
     const int* perm = a.perm;
     const int k = a.k;
-    auto a_row = [&](int r) { return r < rows ? (perm[base + r] / k) * H : -1; };
+    auto a_row = [&](int r) { return (perm[base + r] / k) * H; };  // 0 <= r < rows
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<kBKGate>(acc, X, a_row, rows, codes, scl, brow, H, lds);
+    nv_kloop<kBKGate>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
     const int g = lane >> 4;
@@ -474,7 +524,7 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
 // 64 grouped rows, 256 columns of H); wave w owns columns n0 + 64w .. +64 as
 // 4 column blocks of 16. A rows are contiguous grouped rows of h~.
 __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * (kBKDown + 8)];
+    __shared__ __bf16 lds[2 * 64 * kBKDown];
     int tile, nt;
     if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
@@ -483,19 +533,19 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int n0 = nt * 256 + 64 * wave;
-    const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
-    const uint8_t* codes = blk + (size_t)I * H;                              // down [H][I/2]
-    const uint8_t* scl = blk + (size_t)3 * I * H / 2 + (size_t)2 * I * H / 16;  // down scales [H][I/16]
+    const void* blk = a.expert_ptrs[e];
+    const uint32_t codes_off = (uint32_t)I * H;                                  // down [H][I/2]
+    const uint32_t scl_off = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / 16;  // down scales [H][I/16]
     const int m16 = lane & 15;
     const int brow[4] = {n0 + m16, n0 + 16 + m16, n0 + 32 + m16, n0 + 48 + m16};
     const __bf16* Hq = reinterpret_cast<const __bf16*>(a.a_src);
-    auto a_row = [&](int r) { return r < rows ? (base + r) * I : -1; };
+    auto a_row = [&](int r) { return (base + r) * I; };  // 0 <= r < rows
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<kBKDown>(acc, Hq, a_row, rows, codes, scl, brow, I, lds);
+    nv_kloop<kBKDown>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
@@ -727,7 +777,8 @@ __global__ __launch_bounds__(256) void k_combine_prefill(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-static unsigned grid8(int n) { return (unsigned)((n + 7) / 8 * 8); }
+// grid of the grouped GEMMs (see map_tile): every XCD's M-tiles times NT
+static unsigned gemm_grid(int max_mtiles, int NT) { return (unsigned)(8 * ((max_mtiles + 7) / 8) * NT); }
 
 #define LAUNCH_CHECK()                              \
     do {                                            \
@@ -762,11 +813,14 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
                            reinterpret_cast<bf16x8*>(xq));
         LAUNCH_CHECK();
         ga.a_src = xq; ga.out = L.hq; ga.h_q = dbg ? dbg->h_q : nullptr; ga.NT = I / 128;
-        hipLaunchKernelGGL(k_gateup_nv, dim3(grid8(mt * ga.NT)), dim3(256), 0, s, ga);
+        ga.a_bytes = (uint32_t)((size_t)T * H * 2);
+        ga.block_bytes = (uint32_t)((size_t)3 * H * I / 2 + (size_t)3 * H * I / 16);
+        hipLaunchKernelGGL(k_gateup_nv, dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
         LAUNCH_CHECK();
         GemmArgs gd = ga;
         gd.a_src = L.hq; gd.out = L.Y; gd.h_pre = nullptr; gd.h_q = nullptr; gd.NT = H / 256;
-        hipLaunchKernelGGL(k_down_nv, dim3(grid8(mt * gd.NT)), dim3(256), 0, s, gd);
+        gd.a_bytes = (uint32_t)((size_t)n * I * 2);
+        hipLaunchKernelGGL(k_down_nv, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     } else {
         uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);
@@ -778,10 +832,10 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         ga.a_src = xc; ga.a_scl = xs; ga.out = L.hf;
         if (I % 192 == 0) {
             ga.NT = I / 192;
-            hipLaunchKernelGGL((k_gateup_mx<3, 1>), dim3(grid8(mt * ga.NT)), dim3(256), 0, s, ga);
+            hipLaunchKernelGGL((k_gateup_mx<3, 1>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
         } else {
             ga.NT = I / 64;
-            hipLaunchKernelGGL((k_gateup_mx<1, 4>), dim3(grid8(mt * ga.NT)), dim3(256), 0, s, ga);
+            hipLaunchKernelGGL((k_gateup_mx<1, 4>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
         }
         LAUNCH_CHECK();
         uint8_t* hc = reinterpret_cast<uint8_t*>(L.hq);
@@ -792,7 +846,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         LAUNCH_CHECK();
         GemmArgs gd = ga;
         gd.a_src = hc; gd.a_scl = hs; gd.out = L.Y; gd.h_pre = nullptr; gd.NT = H / 256;
-        hipLaunchKernelGGL(k_down_mx, dim3(grid8(mt * gd.NT)), dim3(256), 0, s, gd);
+        hipLaunchKernelGGL(k_down_mx, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     }
     hipLaunchKernelGGL(k_combine_prefill, dim3((H / 4 + 255) / 256, T), dim3(256), 0, s, L.Y, L.pos, w, k, H, out,

@@ -181,6 +181,9 @@ int moe_expert_prefill(const moe_desc* d, const float* x, int32_t T, const void*
     if (!moe::prefill_supported(d->format, d->H, d->I, d->E, d->k))
         return fail(MOE_ERR_UNSUPPORTED, "no prefill kernel for format=%d H=%d I=%d E=%d k=%d", d->format, d->H, d->I,
                     d->E, d->k);
+    if (!moe::prefill_tokens_supported(d->H, d->I, d->k, T))
+        return fail(MOE_ERR_UNSUPPORTED, "T=%d: the rounded activations would exceed 2 GiB (H=%d I=%d k=%d)", T, d->H,
+                    d->I, d->k);
     if ((r = check_ws(ws, ws_bytes, moe::prefill_ws_bytes(d->format, d->H, d->I, d->E, d->k, T)))) return r;
     moe::PrefillDebug pd = {};
     if (dbg) {

@@ -287,6 +287,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(p)), (short)0,
                                              (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+// Workgroup barrier that orders LDS only: every LDS access before it is done
+// and visible after it, while global loads stay in flight across it (a plain
+// __syncthreads also waits for every outstanding global load, which would
+// drain any prefetch).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The wave's index in its workgroup, as a value the compiler knows is uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ uint32_t ld_b32(rsrc_t r, uint32_t off) {

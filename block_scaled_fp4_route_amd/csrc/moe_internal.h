@@ -53,6 +53,7 @@ hipError_t launch_dequant(int fmt, int H, int I, const void* block, float* gate,
 
 // ---- prefill ----
 bool prefill_supported(int fmt, int H, int I, int E, int k);
+bool prefill_tokens_supported(int H, int I, int k, int T);
 size_t prefill_ws_bytes(int fmt, int H, int I, int E, int k, int T);
 struct PrefillDebug {
     uint16_t* x_bf16;
