@@ -317,6 +317,7 @@ struct GemmArgs {
     float* h_q;             // optional debug (NVFP4)
     int E, H, I, k, NT;     // NT = N-tiles per M-tile
     uint32_t a_bytes;       // bytes of a_src
+    uint32_t a_scl_bytes;   // bytes of a_scl (MXFP4)
     uint32_t block_bytes;   // bytes of one expert block
 };
 
@@ -573,16 +574,17 @@ __global__ __launch_bounds__(256) void k_gateup_mx(GemmArgs a) {
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = min(kBM_MX, a.count[e] - m0);
     const int base = a.off[e] + m0;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int H = a.H, I = a.I, k = a.k;
     const int g = lane >> 4, m16 = lane & 15;
     const int cbase = nt * 64 * NCB + 16 * NCB * wave + m16;
-    const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
-    const uint8_t* scl0 = blk + (size_t)3 * I * H / 2;
-    const uint8_t* xc = reinterpret_cast<const uint8_t*>(a.a_src);
+    const rsrc_t rw = make_rsrc(a.expert_ptrs[e], a.block_bytes);
+    const rsrc_t rx = make_rsrc(a.a_src, a.a_bytes);
+    const rsrc_t rxs = make_rsrc(a.a_scl, a.a_scl_bytes);
+    const uint32_t scl0 = (uint32_t)3 * I * H / 2;
     // A rows of the two row blocks (padding rows read row 0 of the tile:
     // their outputs are discarded)
-    int ar[2];
+    uint32_t ar[2];
 #pragma unroll
     for (int rb = 0; rb < 2; rb++) {
         const int r = 16 * rb + m16;
@@ -595,31 +597,41 @@ __global__ __launch_bounds__(256) void k_gateup_mx(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2 * NCB; j++) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // B rows: j < NCB gate column blocks, j >= NCB up column blocks
+    uint32_t brow[2 * NCB];
+#pragma unroll
+    for (int j = 0; j < 2 * NCB; j++) brow[j] = (uint32_t)(j < NCB ? 0 : I) + cbase + 16 * (j % NCB);
     uint4 bv[2][KU][2 * NCB], av[2][KU][2];
     int sb[2][KU][2 * NCB], sa[2][KU][2];
+    const int nsteps = H / 128;
+    // every group issues the same loads (steps past the end use an
+    // out-of-range offset: zeros, no memory traffic), so the compiler's
+    // memory counter waits stay exact and one group stays in flight while
+    // the other is computed
     auto load = [&](int buf, int kg) {
 #pragma unroll
         for (int u = 0; u < KU; u++) {
-            const int kb = (kg + u) * 128 + 32 * g;
+            const bool on = kg + u < nsteps;
+            const uint32_t kb = (uint32_t)(kg + u) * 128 + 32 * g;
 #pragma unroll
             for (int j = 0; j < 2 * NCB; j++) {
-                const size_t row = (size_t)(j < NCB ? 0 : I) + cbase + 16 * (j % NCB);
-                bv[buf][u][j] = *reinterpret_cast<const uint4*>(blk + row * (H / 2) + kb / 2);
-                sb[buf][u][j] = scl0[row * (H / 32) + kb / 32];
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, on ? brow[j] * (H / 2) + kb / 2 : kOOB, 0, 0);
+                bv[buf][u][j] = uint4{v[0], v[1], v[2], v[3]};
+                sb[buf][u][j] = (int)ld_b8(rw, on ? scl0 + brow[j] * (H / 32) + kb / 32 : kOOB);
             }
 #pragma unroll
             for (int rb = 0; rb < 2; rb++) {
-                av[buf][u][rb] = *reinterpret_cast<const uint4*>(xc + (size_t)ar[rb] * (H / 2) + kb / 2);
-                sa[buf][u][rb] = a.a_scl[(size_t)ar[rb] * (H / 32) + kb / 32];
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, on ? ar[rb] * (H / 2) + kb / 2 : kOOB, 0, 0);
+                av[buf][u][rb] = uint4{v[0], v[1], v[2], v[3]};
+                sa[buf][u][rb] = (int)ld_b8(rxs, on ? ar[rb] * (H / 32) + kb / 32 : kOOB);
             }
         }
     };
-    auto compute = [&](int buf) {
+    auto compute = [&](int buf, int kg) {
 #pragma unroll
         for (int u = 0; u < KU; u++) {
 #pragma unroll
             for (int rb = 0; rb < 2; rb++) {
-                if (rb < nrb) {  // uniform: skip the padding row block of a short tile
+                if (rb < nrb && kg + u < nsteps) {  // uniform: padding row block, steps past the end
                     const uint4 v = av[buf][u][rb];
                     const i32x8 A = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 #pragma unroll
@@ -633,16 +645,14 @@ __global__ __launch_bounds__(256) void k_gateup_mx(GemmArgs a) {
             }
         }
     };
-    const int nsteps = H / 128;  // multiple of 2*KU (H % 512 == 0 is required, KU <= 2)
     // two K groups per iteration so that both register buffers have
     // compile-time indices
     load(0, 0);
     for (int kg = 0; kg < nsteps; kg += 2 * KU) {
-        if (kg + KU < nsteps) load(1, kg + KU);
-        compute(0);
-        if (kg + KU >= nsteps) break;
-        if (kg + 2 * KU < nsteps) load(0, kg + 2 * KU);
-        compute(1);
+        load(1, kg + KU);
+        compute(0, kg);
+        load(0, kg + 2 * KU);
+        compute(1, kg + KU);
     }
     // D layout: lane holds column cbase + 16 j, rows 16 rb + 4 g + i
     float* hf = reinterpret_cast<float*>(a.out);
@@ -671,36 +681,42 @@ __global__ __launch_bounds__(256) void k_down_mx(GemmArgs a) {
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = min(kBM_MX, a.count[e] - m0);
     const int base = a.off[e] + m0;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int H = a.H, I = a.I;
     const int g = lane >> 5, m32 = lane & 31;
-    const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.expert_ptrs[e]);
-    const uint8_t* dcode = blk + (size_t)I * H;
-    const uint8_t* dscl = blk + (size_t)3 * I * H / 2 + (size_t)2 * I * H / 32;
+    const rsrc_t rw = make_rsrc(a.expert_ptrs[e], a.block_bytes);
+    const rsrc_t rh = make_rsrc(a.a_src, a.a_bytes);
+    const rsrc_t rhs = make_rsrc(a.a_scl, a.a_scl_bytes);
+    const uint32_t dcode = (uint32_t)I * H;
+    const uint32_t dscl = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / 32;
     const int n0 = nt * 256 + 64 * wave;
-    const uint8_t* hc = reinterpret_cast<const uint8_t*>(a.a_src);
-    const int arow = base + (m32 < rows ? m32 : 0);
+    const uint32_t arow = base + (m32 < rows ? m32 : 0);
     f32x16 acc[2];
 #pragma unroll
     for (int cb = 0; cb < 2; cb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[cb][i] = 0.f;
-    constexpr int KU = 5;  // I / 64 is a multiple of 5 for I = 2880; tails handled below
+    constexpr int KU = 5;  // K steps per group (I = 2880: 45 steps)
     uint4 av[2][KU], bv[2][KU][2];
     int sa[2][KU], sb[2][KU][2];
     const int nsteps = I / 64;
+    // every group issues the same loads (steps past the end use an
+    // out-of-range offset: zeros, no memory traffic), so that the compiler's
+    // memory counter waits stay exact
     auto load = [&](int buf, int kg) {
 #pragma unroll
         for (int u = 0; u < KU; u++) {
-            const int st = min(kg + u, nsteps - 1);  // clamped: tail steps reload a valid step, not used
-            const int kb = st * 64 + 32 * g;
-            av[buf][u] = *reinterpret_cast<const uint4*>(hc + (size_t)arow * (I / 2) + kb / 2);
-            sa[buf][u] = a.a_scl[(size_t)arow * (I / 32) + kb / 32];
+            const bool on = kg + u < nsteps;
+            const uint32_t kb = (uint32_t)(kg + u) * 64 + 32 * g;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rh, on ? arow * (I / 2) + kb / 2 : kOOB, 0, 0);
+            av[buf][u] = uint4{v[0], v[1], v[2], v[3]};
+            sa[buf][u] = (int)ld_b8(rhs, on ? arow * (I / 32) + kb / 32 : kOOB);
 #pragma unroll
             for (int cb = 0; cb < 2; cb++) {
-                const size_t n = (size_t)n0 + 32 * cb + m32;
-                bv[buf][u][cb] = *reinterpret_cast<const uint4*>(dcode + n * (I / 2) + kb / 2);
-                sb[buf][u][cb] = dscl[n * (I / 32) + kb / 32];
+                const uint32_t n = (uint32_t)n0 + 32 * cb + m32;
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rw, on ? dcode + n * (I / 2) + kb / 2 : kOOB, 0, 0);
+                bv[buf][u][cb] = uint4{w[0], w[1], w[2], w[3]};
+                sb[buf][u][cb] = (int)ld_b8(rw, on ? dscl + n * (I / 32) + kb / 32 : kOOB);
             }
         }
     };
@@ -722,10 +738,9 @@ __global__ __launch_bounds__(256) void k_down_mx(GemmArgs a) {
     };
     load(0, 0);
     for (int kg = 0; kg < nsteps; kg += 2 * KU) {
-        if (kg + KU < nsteps) load(1, kg + KU);
+        load(1, kg + KU);
         compute(0, kg);
-        if (kg + KU >= nsteps) break;
-        if (kg + 2 * KU < nsteps) load(0, kg + 2 * KU);
+        load(0, kg + 2 * KU);
         compute(1, kg + KU);
     }
     // D layout: lane holds column l%32; register i -> row 8(i/4) + 4(l/32) + i%4
@@ -830,9 +845,12 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
                            reinterpret_cast<uint32_t*>(xc), xs, (float*)nullptr);
         LAUNCH_CHECK();
         ga.a_src = xc; ga.a_scl = xs; ga.out = L.hf;
+        ga.a_bytes = (uint32_t)((size_t)T * H / 2);
+        ga.a_scl_bytes = (uint32_t)((size_t)T * H / 32);
+        ga.block_bytes = (uint32_t)((size_t)3 * H * I / 2 + (size_t)3 * H * I / 32);
         if (I % 192 == 0) {
             ga.NT = I / 192;
-            hipLaunchKernelGGL((k_gateup_mx<3, 1>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
+            hipLaunchKernelGGL((k_gateup_mx<3, 2>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
         } else {
             ga.NT = I / 64;
             hipLaunchKernelGGL((k_gateup_mx<1, 4>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
@@ -846,6 +864,8 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         LAUNCH_CHECK();
         GemmArgs gd = ga;
         gd.a_src = hc; gd.a_scl = hs; gd.out = L.Y; gd.h_pre = nullptr; gd.NT = H / 256;
+        gd.a_bytes = (uint32_t)((size_t)n * I / 2);
+        gd.a_scl_bytes = (uint32_t)((size_t)n * I / 32);
         hipLaunchKernelGGL(k_down_mx, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     }
