@@ -39,6 +39,7 @@ struct PrefillWs {
     int* tile_e;  // [max_tiles]
     int* tile_m;  // [max_tiles] first row of the tile within its expert
     int* ntiles;  // [1]
+    void* rec;    // [max_tiles] TileRec (MXFP4 GEMMs)
     void* xq;     // x~: bf16 [T][H] | MXFP4 codes [T][H/2] + scales [T][H/32]
     void* hq;     // h~: bf16 [T*k][I] | MXFP4 codes [T*k][I/2] + scales [T*k][I/32]
     float* hf;    // MXFP4 only: h before rounding [T*k][I]
@@ -65,6 +66,7 @@ static PrefillWs prefill_layout(int fmt, int H, int I, int E, int k, int T, void
     w.tile_e = (int*)take(sizeof(int) * mt);
     w.tile_m = (int*)take(sizeof(int) * mt);
     w.ntiles = (int*)take(sizeof(int));
+    w.rec = take(16 * (size_t)mt);
     if (fmt == kFmtNvfp4) {
         w.xq = take((size_t)T * H * 2);
         w.hq = take(n * I * 2);
@@ -167,9 +169,23 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
 // ---------------------------------------------------------------------------
 // 2. tile list: experts ordered by row count (descending; ties by index),
 // each split into M-tiles of BM rows.
+//
+// With rec != nullptr it also writes one record per slot of the max_tiles
+// slots: the expert block, the first grouped row and the row count of the
+// tile (row count 0 for slots past the last tile), so a GEMM workgroup finds
+// everything it needs with one load.
+struct TileRec {
+    const uint8_t* blk;  // expert block
+    int base;            // first grouped row
+    int rows;            // rows of the tile; 0: no tile in this slot
+};
+static_assert(sizeof(TileRec) == 16, "tile record is 16 bytes");
+
 __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restrict__ count, int E, int BM,
                                                              int* __restrict__ tile_e, int* __restrict__ tile_m,
-                                                             int* __restrict__ ntiles) {
+                                                             int* __restrict__ ntiles, TileRec* __restrict__ rec,
+                                                             int max_slots, const int* __restrict__ off,
+                                                             const void* const* __restrict__ expert_ptrs) {
     __shared__ int cnt[kMaxE];
     __shared__ int nt_sorted[kMaxE];
     __shared__ int ex_sorted[kMaxE];
@@ -202,6 +218,23 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
         for (int m = 0; m < nt_sorted[r]; m++) {
             tile_e[start[r] + m] = e;
             tile_m[start[r] + m] = m * BM;
+            if (rec) {
+                TileRec t;
+                t.blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
+                t.base = off[e] + m * BM;
+                t.rows = min(BM, cnt[e] - m * BM);
+                rec[start[r] + m] = t;
+            }
+        }
+    }
+    if (rec) {
+        const int used = start[kGroupThreads];
+        for (int i = used + tid; i < max_slots; i += kGroupThreads) {
+            TileRec t;
+            t.blk = nullptr;
+            t.base = 0;
+            t.rows = 0;
+            rec[i] = t;
         }
     }
 }
@@ -319,6 +352,8 @@ struct GemmArgs {
     uint32_t a_bytes;       // bytes of a_src
     uint32_t a_scl_bytes;   // bytes of a_scl (MXFP4)
     uint32_t block_bytes;   // bytes of one expert block
+    const TileRec* rec;     // MXFP4: tile records
+    int mt;                 // MXFP4: record slots
 };
 
 // Wait until at most N vector memory operations of this wave are outstanding
@@ -366,6 +401,16 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 // consecutive rows on distinct bank groups. Rows past `rows` load row 0
 // (their sums are never stored).
 constexpr uint32_t kOOB = 0x7FFFFFF0u;  // beyond every buffer here: loads return 0
+
+// 16-byte buffer load straight into LDS: lane l writes lds + 16*l (lds is
+// wave-uniform).
+__device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+// Compiler ordering point: memory accesses stay on their side of it, and
+// code that uses a or b after it cannot be scheduled before it.
+__device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
 template <int BK, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, uint32_t a_bytes,
@@ -561,197 +606,289 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 4c. MXFP4 gate/up with the scaled FP4 MFMA (16x16x128): workgroup = (M-tile
-// of 32 rows = 2 row blocks, 64*NCB output columns of I); wave w owns NCB
-// column blocks of 16 of gate and of up, so one activation fragment feeds
-// 2*NCB MFMAs. Lane l holds row/column l%16 and K = k0 + 32(l/16) .. +31:
-// 16 code bytes plus one UE8M0 scale byte, read straight from x~ and from
-// the weight rows. KU K-steps of loads are in flight ahead of the MFMAs.
-template <int NCB, int KU>
-__global__ __launch_bounds__(256) void k_gateup_mx(GemmArgs a) {
-    int tile, nt;
-    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
-    const int e = a.tile_e[tile], m0 = a.tile_m[tile];
-    const int rows = min(kBM_MX, a.count[e] - m0);
-    const int base = a.off[e] + m0;
+// 4c. MXFP4 grouped GEMMs: v_mfma_scale_f32_16x16x128_f8f6f4 on the e2m1
+// codes of both operands with their UE8M0 block scales ([D] "Making it
+// faster": the FP4 weights go to the matrix cores as they are, never
+// widened). With a few tokens per expert these GEMMs stream the expert
+// weights once, so the kernel is built around reading weight rows the way
+// HBM likes best: whole row segments, contiguous.
+//
+// Workgroup = (tile of <= 32 grouped rows of one expert, 64 weight rows).
+// gate/up (GU): weight rows 0..31 are gate rows c0..c0+31, rows 32..63 the
+// up rows of the same columns, so SiLU*mul pairs stay in the workgroup;
+// down: weight rows n0..n0+63 of Wd.
+// The weight rows go through an LDS ring of NBUF chunk buffers, CB bytes of
+// every row per chunk, with buffer_load ... lds (16 bytes per lane, no
+// registers): one instruction covers 1024/CB rows, CB contiguous bytes each.
+// Piece p (16 bytes = one 32-code MX block) of row r sits at slot
+// r*SPR + (p ^ (r & 15)), so the 16 rows of an MFMA operand read (one piece
+// each) fall on distinct bank groups. The block scales of the 64 rows are
+// loaded once into LDS at the start.
+// K split: the four waves take different K steps of every chunk (SPW steps
+// of 128 each) for all 64 rows and both row blocks, so every activation
+// fragment is loaded once per workgroup; the partial sums meet in LDS at the
+// end. Activation fragments (A: lane = row l%16, 32 codes of K slot l/16 and
+// their scale byte) are read straight from x~/h~ with buffer loads.
+// The dot product does not depend on the order of K, so K slot g of the step
+// (c, w, t) is MX block b = c*SPR + 4*(w*SPW + t) + g for both operands.
+// Blocks past the end of the row (b >= K/32) load A from an out-of-range
+// offset (zero codes, scale byte 0) and clamp the B scale to the last block
+// of the row, so they add exact zeros.
+// Pipeline: chunk group j = (weight chunk j, A fragments of chunk j) is
+// issued NBUF-1 chunks ahead; every group has the same loads (out-of-range
+// past the end), so "group c has landed" is a fixed count of younger loads.
+// Each ring buffer is its own LDS array, so the compiler's own waits before
+// an LDS read only cover the loads into that buffer.
+template <bool GU, int CB, int NBUF, int SCLB>
+__global__ __launch_bounds__(256) void k_mx_stream(GemmArgs a) {
+    constexpr int SPR = CB / 16;        // pieces (MX blocks) per row per chunk
+    constexpr int CKB = 64 * CB;        // bytes per ring buffer
+    constexpr int NI = CKB / 1024 / 4;  // weight loads per wave per chunk
+    constexpr int SPW = CB / 256;       // K steps of 128 per wave per chunk
+    constexpr int NA = 2 * (SPW + 1);   // activation loads per wave per chunk (2 row blocks)
+    static_assert(NBUF >= 2 && NBUF <= 4 && (SPW == 1 || SPW == 2) && SPR >= 16, "ring shape");
+    static_assert(!GU || SPW == 2, "gate/up streams 512-byte row chunks");
+    static_assert(GU || SPW == 1, "down streams 256-byte row chunks");
+    __shared__ __attribute__((aligned(16))) uint8_t q0[CKB];
+    __shared__ __attribute__((aligned(16))) uint8_t q1[CKB];
+    __shared__ __attribute__((aligned(16))) uint8_t q2[NBUF > 2 ? CKB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t q3[NBUF > 3 ? CKB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t scl[SCLB];
+    uint8_t* const ring[4] = {q0, q1, q2, q3};
+
+    // workgroup -> (tile, N-tile): see map_tile
+    const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8;
+    const int tile = xcd + 8 * (jj / a.NT), nt = jj % a.NT;
+    if (tile >= a.mt) return;
+    const TileRec tr = a.rec[tile];
+    if (tr.rows <= 0) return;
+    const int rows = tr.rows, base = tr.base;
+    const int nrb = rows > 16 ? 2 : 1;
+
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int H = a.H, I = a.I, k = a.k;
     const int g = lane >> 4, m16 = lane & 15;
-    const int cbase = nt * 64 * NCB + 16 * NCB * wave + m16;
-    const rsrc_t rw = make_rsrc(a.expert_ptrs[e], a.block_bytes);
+    const int H = a.H, I = a.I;
+    const uint32_t KB = GU ? (uint32_t)H / 2 : (uint32_t)I / 2;  // code bytes per weight row
+    const uint32_t SB = KB / 16;                                // scale bytes per row = MX blocks per row
+    const int nch = (int)((KB + CB - 1) / CB);
+    const int c0 = GU ? 32 * nt : 64 * nt;  // first output column (GU: of I; down: of H)
+
+    const rsrc_t rw = make_rsrc(tr.blk, a.block_bytes);
     const rsrc_t rx = make_rsrc(a.a_src, a.a_bytes);
     const rsrc_t rxs = make_rsrc(a.a_scl, a.a_scl_bytes);
-    const uint32_t scl0 = (uint32_t)3 * I * H / 2;
-    // A rows of the two row blocks (padding rows read row 0 of the tile:
-    // their outputs are discarded)
-    uint32_t ar[2];
+
+    // activation rows of the two row blocks (rows past the tile read its
+    // first row; their sums are never stored). GU rows come from perm: the
+    // loads are issued here, the row offsets formed after the first weight
+    // loads are out (see the prologue).
+    int arow[2];
 #pragma unroll
     for (int rb = 0; rb < 2; rb++) {
-        const int r = 16 * rb + m16;
-        ar[rb] = a.perm[base + (r < rows ? r : 0)] / k;
+        const int m = 16 * rb + m16;
+        const int r = m < rows ? m : 0;
+        arow[rb] = GU ? a.perm[base + r] : base + r;
     }
-    const int nrb = rows > 16 ? 2 : 1;  // wave-uniform
-    f32x4 acc[2][2 * NCB];
+    uint32_t aoff[2], asoff[2];
+    auto set_rows = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-        for (int j = 0; j < 2 * NCB; j++) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // B rows: j < NCB gate column blocks, j >= NCB up column blocks
-    uint32_t brow[2 * NCB];
-#pragma unroll
-    for (int j = 0; j < 2 * NCB; j++) brow[j] = (uint32_t)(j < NCB ? 0 : I) + cbase + 16 * (j % NCB);
-    uint4 bv[2][KU][2 * NCB], av[2][KU][2];
-    int sb[2][KU][2 * NCB], sa[2][KU][2];
-    const int nsteps = H / 128;
-    // every group issues the same loads (steps past the end use an
-    // out-of-range offset: zeros, no memory traffic), so the compiler's
-    // memory counter waits stay exact and one group stays in flight while
-    // the other is computed
-    auto load = [&](int buf, int kg) {
-#pragma unroll
-        for (int u = 0; u < KU; u++) {
-            const bool on = kg + u < nsteps;
-            const uint32_t kb = (uint32_t)(kg + u) * 128 + 32 * g;
-#pragma unroll
-            for (int j = 0; j < 2 * NCB; j++) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, on ? brow[j] * (H / 2) + kb / 2 : kOOB, 0, 0);
-                bv[buf][u][j] = uint4{v[0], v[1], v[2], v[3]};
-                sb[buf][u][j] = (int)ld_b8(rw, on ? scl0 + brow[j] * (H / 32) + kb / 32 : kOOB);
+        for (int rb = 0; rb < 2; rb++) {
+            const uint32_t ar = GU ? (uint32_t)(arow[rb] / a.k) : (uint32_t)arow[rb];
+            aoff[rb] = ar * KB;
+            asoff[rb] = ar * SB;
+        }
+    };
+
+    // scales of the 64 weight rows -> scl: [64][SB]; GU rows are 16-byte
+    // pieces, piece p of row r stored at r*PPR + (p ^ (r & smask)); down rows
+    // (SB bytes, any even count) are stored as they are.
+    const uint32_t code0 = GU ? 0u : (uint32_t)I * H;
+    const uint32_t PPR = SB / 16;
+    const uint32_t smask = GU ? (min(PPR & (~PPR + 1u), 8u) - 1u) : 0u;
+    {
+        const uint32_t sbase = (uint32_t)3 * I * H / 2;
+        const uint32_t nsl = (64 * SB + 1023) / 1024;  // 1 KB loads for the whole area
+        for (uint32_t ii = wave; ii < nsl; ii += 4) {
+            uint32_t o;
+            if (GU) {
+                const uint32_t P = ii * 64 + lane, r = P / PPR, sp = P % PPR, p = sp ^ (r & smask);
+                const uint32_t row = (r < 32 ? 0u : (uint32_t)I) + c0 + (r & 31);
+                o = r < 64 ? sbase + row * SB + 16 * p : kOOB;
+            } else {
+                const uint32_t b = ii * 1024 + 16 * lane;
+                o = b < 64 * SB ? sbase + (uint32_t)2 * I * H / 32 + (uint32_t)c0 * SB + b : kOOB;
             }
+            load_lds16(rw, scl + ii * 1024, o);
+        }
+    }
+    // (these loads are older than chunk group 0, so the wait for group 0
+    // covers them)
+
+    // this lane's weight loads: ring slot q = (wave*NI + i)*64 + lane
+    uint32_t woff[NI], wcol[NI];
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, on ? ar[rb] * (H / 2) + kb / 2 : kOOB, 0, 0);
-                av[buf][u][rb] = uint4{v[0], v[1], v[2], v[3]};
-                sa[buf][u][rb] = (int)ld_b8(rxs, on ? ar[rb] * (H / 32) + kb / 32 : kOOB);
+    for (int i = 0; i < NI; i++) {
+        const uint32_t q = (uint32_t)(wave * NI + i) * 64 + lane, r = q / SPR, sp = q % SPR, p = sp ^ (r & 15u);
+        const uint32_t row = GU ? (r < 32 ? 0u : (uint32_t)I) + c0 + (r & 31) : (uint32_t)c0 + r;
+        wcol[i] = 16 * p;
+        woff[i] = code0 + row * KB + 16 * p;
+    }
+
+    // register sets for the activation fragments of NBUF chunks
+    uint4 av[NBUF][2][SPW];
+    uint32_t as[NBUF][2][SPW];
+    auto issue_w = [&](int c, int u) {
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const bool on = c < nch && (uint32_t)c * CB + wcol[i] < KB;
+            load_lds16(rw, ring[u] + (wave * NI + i) * 1024, on ? woff[i] + (uint32_t)c * CB : kOOB);
+        }
+    };
+    auto issue_a = [&](int c, int u) {
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const bool onr = rb < nrb && c < nch;
+#pragma unroll
+            for (int t = 0; t < SPW; t++) {
+                const uint32_t b = (uint32_t)c * SPR + 4 * (wave * SPW + t) + g;
+                const bool on = onr && b < SB;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, on ? aoff[rb] + 16 * b : kOOB, 0, 0);
+                av[u][rb][t] = uint4{v[0], v[1], v[2], v[3]};
+            }
+            if constexpr (SPW == 2) {
+                // the 8 scale bytes of the wave's two steps (SB is a multiple of 16)
+                const uint32_t b0 = (uint32_t)c * SPR + 8 * wave;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rxs, onr && b0 < SB ? asoff[rb] + b0 : kOOB, 0, 0);
+                as[u][rb][0] = (v[0] >> (8 * g)) & 0xFFu;
+                as[u][rb][1] = (v[1] >> (8 * g)) & 0xFFu;
+            } else {
+                const uint32_t b = (uint32_t)c * SPR + 4 * wave + g;
+                as[u][rb][0] = ld_b8(rxs, onr && b < SB ? asoff[rb] + b : kOOB);
             }
         }
     };
-    auto compute = [&](int buf, int kg) {
+
+    f32x4 acc[2][4];
 #pragma unroll
-        for (int u = 0; u < KU; u++) {
+    for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                if (rb < nrb && kg + u < nsteps) {  // uniform: padding row block, steps past the end
-                    const uint4 v = av[buf][u][rb];
-                    const i32x8 A = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        for (int j = 0; j < 4; j++) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c, int u) {
+        const uint8_t* B = ring[u];
 #pragma unroll
-                    for (int j = 0; j < 2 * NCB; j++) {
-                        const uint4 w = bv[buf][u][j];
-                        const i32x8 B = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-                        acc[rb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[rb][j], 4, 4, 0,
-                                                                                      sa[buf][u][rb], 0, sb[buf][u][j]);
+        for (int t = 0; t < SPW; t++) {
+            const uint32_t bfirst = (uint32_t)c * SPR + 4 * (wave * SPW + t);
+            if (c < nch && bfirst < SB) {  // uniform: steps wholly past the row end add nothing
+                const uint32_t p = 4 * (wave * SPW + t) + g;  // piece within the chunk
+                const uint32_t b = min(bfirst + g, SB - 1);  // scale of the block (clamped)
+                i32x8 Bf[4];
+                int sb[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t r = 16 * j + m16;
+                    const uint4 w = *reinterpret_cast<const uint4*>(B + (r * SPR + (p ^ (r & 15u))) * 16);
+                    Bf[j] = i32x8{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+                    uint32_t so;
+                    if (GU) {
+                        const uint32_t pp = b / 16;
+                        so = r * SB + 16 * (pp ^ (r & smask)) + (b & 15);
+                    } else {
+                        so = r * SB + b;
+                    }
+                    sb[j] = scl[so];
+                }
+#pragma unroll
+                for (int rb = 0; rb < 2; rb++) {
+                    if (rb < nrb) {  // uniform
+                        const uint4 v = av[u][rb][t];
+                        const i32x8 A = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            acc[rb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                A, Bf[j], acc[rb][j], 4, 4, 0, (int)as[u][rb][t], 0, sb[j]);
                     }
                 }
             }
         }
     };
-    // two K groups per iteration so that both register buffers have
-    // compile-time indices
-    load(0, 0);
-    for (int kg = 0; kg < nsteps; kg += 2 * KU) {
-        load(1, kg + KU);
-        compute(0, kg);
-        load(0, kg + 2 * KU);
-        compute(1, kg + KU);
+
+    // prologue: groups 0 .. NBUF-2. The asm statements keep the groups in
+    // order, and keep the row offsets (which wait for the perm loads) behind
+    // the first weight loads.
+    issue_w(0, 0);
+    order_point(arow[0], arow[1]);
+    set_rows();
+    issue_a(0, 0);
+#pragma unroll
+    for (int j = 1; j < NBUF - 1; j++) {
+        asm volatile("" ::: "memory");
+        issue_w(j, j);
+        issue_a(j, j);
     }
-    // D layout: lane holds column cbase + 16 j, rows 16 rb + 4 g + i
-    float* hf = reinterpret_cast<float*>(a.out);
+    for (int cc = 0; cc < nch; cc += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; u++) {
+            const int c = cc + u;
+            // group c landed in every wave; every wave is done with chunk c-1,
+            // whose buffer group c+NBUF-1 overwrites
+            vm_wait_barrier<(NBUF - 2) * (NI + NA)>();
+            issue_w(c + NBUF - 1, (u + NBUF - 1) % NBUF);
+            issue_a(c + NBUF - 1, (u + NBUF - 1) % NBUF);
+            compute(c, u);
+        }
+    }
+    vm_wait_barrier<0>();  // no load (out-of-range tail groups included) still writes LDS
+
+    // partial sums of the four waves -> LDS (8 KB per wave), then the sums
+    uint8_t* red = CKB >= 32768 ? q0 + wave * 8192 : (wave < 2 ? q0 + wave * 8192 : q1 + (wave - 2) * 8192);
 #pragma unroll
     for (int rb = 0; rb < 2; rb++)
+        if (rb < nrb)
 #pragma unroll
-        for (int j = 0; j < NCB; j++)
+            for (int j = 0; j < 4; j++)
+                *reinterpret_cast<f32x4*>(red + ((rb * 4 + j) * 64 + lane) * 16) = acc[rb][j];
+    __syncthreads();
+    auto part = [&](int w, int rb, int j) -> f32x4 {
+        const uint8_t* rw8 = CKB >= 32768 ? q0 + w * 8192 : (w < 2 ? q0 + w * 8192 : q1 + (w - 2) * 8192);
+        return *reinterpret_cast<const f32x4*>(rw8 + ((rb * 4 + j) * 64 + lane) * 16);
+    };
+    const int rb = wave >> 1;
+    if (rb >= nrb) return;
+    if (GU) {
+        // thread: row block rb, gate column block cj (0/1) and its up block
+        const int cj = wave & 1;
+        f32x4 gs = part(0, rb, cj), us = part(0, rb, cj + 2);
+#pragma unroll
+        for (int w = 1; w < 4; w++) {
+            gs += part(w, rb, cj);
+            us += part(w, rb, cj + 2);
+        }
+        float* hf = reinterpret_cast<float*>(a.out);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = 16 * rb + 4 * g + i;
+            if (r < rows) {
+                const float hv = silu_mul(gs[i], us[i]);
+                const size_t o = (size_t)(base + r) * I + c0 + 16 * cj + m16;
+                hf[o] = hv;
+                if (a.h_pre) a.h_pre[o] = hv;
+            }
+        }
+    } else {
+        float* Y = reinterpret_cast<float*>(a.out);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int j = 2 * (wave & 1) + h;
+            f32x4 ys = part(0, rb, j);
+#pragma unroll
+            for (int w = 1; w < 4; w++) ys += part(w, rb, j);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int r = 16 * rb + 4 * g + i;
-                if (r < rows) {
-                    const float hv = silu_mul(acc[rb][j][i], acc[rb][NCB + j][i]);
-                    const size_t o = (size_t)(base + r) * I + cbase + 16 * j;
-                    hf[o] = hv;
-                    if (a.h_pre) a.h_pre[o] = hv;
-                }
-            }
-}
-
-// 4d. MXFP4 down with the scaled FP4 MFMA (32x32x64): workgroup = (M-tile of
-// 32 grouped rows, 256 columns of H); wave w owns 2 column blocks of 32.
-// Lane l holds row/column l%32 and K = k0 + 32(l/32) .. +31.
-__global__ __launch_bounds__(256) void k_down_mx(GemmArgs a) {
-    int tile, nt;
-    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
-    const int e = a.tile_e[tile], m0 = a.tile_m[tile];
-    const int rows = min(kBM_MX, a.count[e] - m0);
-    const int base = a.off[e] + m0;
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int H = a.H, I = a.I;
-    const int g = lane >> 5, m32 = lane & 31;
-    const rsrc_t rw = make_rsrc(a.expert_ptrs[e], a.block_bytes);
-    const rsrc_t rh = make_rsrc(a.a_src, a.a_bytes);
-    const rsrc_t rhs = make_rsrc(a.a_scl, a.a_scl_bytes);
-    const uint32_t dcode = (uint32_t)I * H;
-    const uint32_t dscl = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / 32;
-    const int n0 = nt * 256 + 64 * wave;
-    const uint32_t arow = base + (m32 < rows ? m32 : 0);
-    f32x16 acc[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[cb][i] = 0.f;
-    constexpr int KU = 5;  // K steps per group (I = 2880: 45 steps)
-    uint4 av[2][KU], bv[2][KU][2];
-    int sa[2][KU], sb[2][KU][2];
-    const int nsteps = I / 64;
-    // every group issues the same loads (steps past the end use an
-    // out-of-range offset: zeros, no memory traffic), so that the compiler's
-    // memory counter waits stay exact
-    auto load = [&](int buf, int kg) {
-#pragma unroll
-        for (int u = 0; u < KU; u++) {
-            const bool on = kg + u < nsteps;
-            const uint32_t kb = (uint32_t)(kg + u) * 64 + 32 * g;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rh, on ? arow * (I / 2) + kb / 2 : kOOB, 0, 0);
-            av[buf][u] = uint4{v[0], v[1], v[2], v[3]};
-            sa[buf][u] = (int)ld_b8(rhs, on ? arow * (I / 32) + kb / 32 : kOOB);
-#pragma unroll
-            for (int cb = 0; cb < 2; cb++) {
-                const uint32_t n = (uint32_t)n0 + 32 * cb + m32;
-                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rw, on ? dcode + n * (I / 2) + kb / 2 : kOOB, 0, 0);
-                bv[buf][u][cb] = uint4{w[0], w[1], w[2], w[3]};
-                sb[buf][u][cb] = (int)ld_b8(rw, on ? dscl + n * (I / 32) + kb / 32 : kOOB);
+                if (r < rows) Y[(size_t)(base + r) * H + c0 + 16 * j + m16] = ys[i];
             }
         }
-    };
-    auto compute = [&](int buf, int kg) {
-#pragma unroll
-        for (int u = 0; u < KU; u++) {
-            if (kg + u < nsteps) {
-                const uint4 v = av[buf][u];
-                const i32x8 A = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-#pragma unroll
-                for (int cb = 0; cb < 2; cb++) {
-                    const uint4 w = bv[buf][u][cb];
-                    const i32x8 B = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-                    acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[cb], 4, 4, 0, sa[buf][u], 0,
-                                                                              sb[buf][u][cb]);
-                }
-            }
-        }
-    };
-    load(0, 0);
-    for (int kg = 0; kg < nsteps; kg += 2 * KU) {
-        load(1, kg + KU);
-        compute(0, kg);
-        load(0, kg + 2 * KU);
-        compute(1, kg + KU);
     }
-    // D layout: lane holds column l%32; register i -> row 8(i/4) + 4(l/32) + i%4
-    float* Y = reinterpret_cast<float*>(a.out);
-#pragma unroll
-    for (int cb = 0; cb < 2; cb++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int r = 8 * (i / 4) + 4 * g + (i % 4);
-            if (r < rows) Y[(size_t)(base + r) * H + n0 + 32 * cb + m32] = acc[cb][i];
-        }
 }
 
 // ---------------------------------------------------------------------------
@@ -813,7 +950,9 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
 
     hipLaunchKernelGGL(k_group, dim3(E), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
     LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, L.tile_e, L.tile_m, L.ntiles);
+    TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
+    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, L.tile_e, L.tile_m, L.ntiles,
+                       rec, mt, off, expert_ptrs);
     LAUNCH_CHECK();
 
     GemmArgs ga = {};
@@ -848,13 +987,13 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         ga.a_bytes = (uint32_t)((size_t)T * H / 2);
         ga.a_scl_bytes = (uint32_t)((size_t)T * H / 32);
         ga.block_bytes = (uint32_t)((size_t)3 * H * I / 2 + (size_t)3 * H * I / 32);
-        if (I % 192 == 0) {
-            ga.NT = I / 192;
-            hipLaunchKernelGGL((k_gateup_mx<3, 2>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
-        } else {
-            ga.NT = I / 64;
-            hipLaunchKernelGGL((k_gateup_mx<1, 4>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
-        }
+        ga.rec = rec;
+        ga.mt = mt;
+        ga.NT = I / 32;
+        if (2 * H <= 8192)
+            hipLaunchKernelGGL((k_mx_stream<true, 512, 2, 8192>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
+        else
+            hipLaunchKernelGGL((k_mx_stream<true, 512, 2, 32768>), dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
         LAUNCH_CHECK();
         uint8_t* hc = reinterpret_cast<uint8_t*>(L.hq);
         uint8_t* hs = hc + (size_t)n * I / 2;
@@ -863,10 +1002,14 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
                            reinterpret_cast<uint32_t*>(hc), hs, dbg ? dbg->h_q : (float*)nullptr);
         LAUNCH_CHECK();
         GemmArgs gd = ga;
-        gd.a_src = hc; gd.a_scl = hs; gd.out = L.Y; gd.h_pre = nullptr; gd.NT = H / 256;
+        gd.a_src = hc; gd.a_scl = hs; gd.out = L.Y; gd.h_pre = nullptr;
         gd.a_bytes = (uint32_t)((size_t)n * I / 2);
         gd.a_scl_bytes = (uint32_t)((size_t)n * I / 32);
-        hipLaunchKernelGGL(k_down_mx, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+        gd.NT = H / 64;
+        if (2 * I <= 8192)
+            hipLaunchKernelGGL((k_mx_stream<false, 256, 4, 8192>), dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+        else
+            hipLaunchKernelGGL((k_mx_stream<false, 256, 4, 32768>), dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     }
     hipLaunchKernelGGL(k_combine_prefill, dim3((H / 4 + 255) / 256, T), dim3(256), 0, s, L.Y, L.pos, w, k, H, out,

@@ -216,6 +216,14 @@ def test_prefill_mxfp4_deepseek_shape_small_E(m, orc):
     full_check(m, orc, wl, 20)
 
 
+@pytest.mark.parametrize("H,I,E,k,T", [(4608, 320, 6, 3, 40), (1536, 4160, 4, 2, 33)])
+def test_prefill_mxfp4_odd_shapes(m, orc, H, I, E, k, T):
+    """Hidden sizes whose weight rows end inside a streamed chunk (4608) or
+    whose scale rows are 3 pieces of 16 bytes (1536), and scale areas past
+    8 KB per 64 weight rows (H 4608 for gate/up, I 4160 for down)."""
+    full_check(m, orc, wl_small("mxfp4", H, I, E, k, T), T)
+
+
 def test_prefill_qwen_full_size_sampled(m, orc):
     """Qwen-shaped prefill at full size (512 experts, 2451 tokens, Zipf 1.1);
     the oracle checks a sample of tokens, including ones on the hottest expert."""
