@@ -35,7 +35,9 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain 1 GiB copy gives),
 # per workload; absent until counters were taken on the current kernels.
 # qwen_decode: k_gateup<1,5,4> + k_down_combine<1,16,5,true,true>.
-TRAFFIC: dict = {"qwen_decode": 38345216}
+# deepseek_prefill: every kernel of one moe_expert_prefill call (group,
+# tile_list, quant_mx x2, k_mx_stream gate/up and down, combine).
+TRAFFIC: dict = {"qwen_decode": 38322240, "deepseek_prefill": 7291975115}
 
 
 def log(*a):
@@ -316,7 +318,7 @@ def run_prefill(args, m, sg, torch):
                    "out": "bf16" if wl.out_bf16 else "f32", "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "moe_expert_prefill (grouping + quantise + grouped GEMMs + combine)",
                      "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": int(byts),
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": TRAFFIC.get(wl.name), "bytes_per_launch": int(byts),
                      "avg_us": round(ms * 1e3, 2)},
         "mfma_TFLOPs": round(tflops, 2), "mfma_peak_TFLOPs": mfma_peak,
         "mfma_frac": round(tflops / mfma_peak, 4), "flops_per_call": flops,

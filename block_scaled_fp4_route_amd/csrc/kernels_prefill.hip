@@ -10,8 +10,9 @@
 //  3. k_quant_x_*: x~ = bf16(x) (NVFP4 layers) or MXFP4 per 32 (MXFP4 layers).
 //  4. ragged grouped GEMMs (gate/up with SiLU*mul epilogue, then down):
 //     NVFP4 weights are decoded to bf16 in registers and multiplied with
-//     v_mfma_f32_16x16x32_bf16; MXFP4 weights and activations go straight into
-//     v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 with their E8M0 scales.
+//     v_mfma_f32_16x16x32_bf16; MXFP4 weights (streamed through an LDS ring)
+//     and activations go straight into v_mfma_scale_f32_16x16x128_f8f6f4
+//     with their E8M0 scales.
 //  5. k_combine: out[t] = sum_j w[t][j] * Y[pos(t, j)] in increasing j.
 #include "moe_device.h"
 #include "moe_internal.h"
