@@ -602,6 +602,344 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
 }
 
 // ----------------------------------------------------------------------------
+// Streaming forms for large layers. When the chosen experts' weights are
+// many times what one round of resident workgroups has in flight, the
+// one-shot tiles above run in several rounds, each paying the full memory
+// latency. Here a resident grid keeps loads in flight continuously instead.
+// A wave covers a weight row with all 64 lanes: lane l reads the 16-byte
+// chunks c = l + 64m (32 codes each), so every load instruction reads 1 KB
+// of one row contiguously, and the wave keeps the activations of its chunks
+// (x, or one hidden vector) in registers for every row it reads.
+constexpr int kStreamDP = 4;  // gate/up row pairs in flight per wave
+constexpr int kStreamRows = 8;  // down rows per workgroup
+
+__device__ __forceinline__ uint32_t ld_b16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// sum over the 32 codes of chunk w (16 bytes) times x[0..31], with the
+// chunk's scales: NVFP4 two E4M3 bytes (16 codes each) applied to the two
+// partial sums; MXFP4 one UE8M0 byte, handed to the e2m1 conversion itself
+// (it multiplies by 2^(byte - 127) exactly: the byte is the exponent field
+// of its fp32 scale operand), so the products need no separate scaling.
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(const uint4& w, uint32_t sc, const float* x, float acc) {
+    if constexpr (FMT == kFmtNvfp4) {
+        acc = fmaf(e4m3_to_f32(sc & 0xFFu), dot16_fp4(w.x, w.y, x), acc);
+        return fmaf(e4m3_to_f32((sc >> 8) & 0xFFu), dot16_fp4(w.z, w.w, x + 16), acc);
+    } else {
+        const float s = __uint_as_float((sc & 0xFFu) << 23);
+        const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], s, 0);
+            const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], s, 1);
+            const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], s, 2);
+            const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], s, 3);
+            acc = fmaf(p0.x, x[8 * i + 0], acc); acc = fmaf(p0.y, x[8 * i + 1], acc);
+            acc = fmaf(p1.x, x[8 * i + 2], acc); acc = fmaf(p1.y, x[8 * i + 3], acc);
+            acc = fmaf(p2.x, x[8 * i + 4], acc); acc = fmaf(p2.y, x[8 * i + 5], acc);
+            acc = fmaf(p3.x, x[8 * i + 6], acc); acc = fmaf(p3.y, x[8 * i + 7], acc);
+        }
+        return acc;
+    }
+}
+
+// this lane's activations of chunks lane + 64m: xs[m][0..31] = v[32c ..]
+template <int NCH>
+__device__ __forceinline__ void load_chunk_acts(const float* v, int nchunk, float (&xs)[NCH][32]) {
+    const f4v* v4 = reinterpret_cast<const f4v*>(v);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int m = 0; m < NCH; m++) {
+        const int c = min(lane + 64 * m, nchunk - 1);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const f4v t = v4[8 * c + i];
+            xs[m][4 * i] = t.x; xs[m][4 * i + 1] = t.y; xs[m][4 * i + 2] = t.z; xs[m][4 * i + 3] = t.w;
+        }
+    }
+}
+
+// cache policy of the weight loads: non-temporal (each weight byte is read
+// once per call)
+constexpr int kNT = 2;
+
+// c ? a : b as integer arithmetic (the compiler turns some conditionals on
+// lane-dependent values into branches)
+__device__ __forceinline__ uint32_t sel_u32(bool c, uint32_t a, uint32_t b) {
+    const uint32_t m = 0u - (uint32_t)c;
+    return (a & m) | (b & ~m);
+}
+// marks a loaded value as used (the compiler then waits for its load here)
+__device__ __forceinline__ void consume(const uint4& v) {
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+__device__ __forceinline__ void consume(uint32_t v) { asm volatile("" ::"v"(v)); }
+
+// gate/up + SiLU*mul, streaming. Units u = slot * I + row (gate row and up
+// row of one routed slot) are split into contiguous ranges, one per
+// workgroup of the grid (sized to be resident at once); wave w takes units
+// w, w + 4, ... of its workgroup's range, so the four waves sweep adjacent
+// rows together, and keeps kStreamDP units of loads in flight. The scales
+// of a unit come with one dword per lane (MXFP4: lanes 0-31 the gate row's,
+// 32-63 the up row's; NVFP4: one dword of each row) and reach the lanes that
+// need them by ds_bpermute. TOPK (moe_layer_decode): the workgroup first
+// selects the experts of the slots its range touches from the logits; the
+// last workgroup, whose range ends with the last slot, publishes the
+// routing. Otherwise (moe_expert_decode) the routing is given and workgroup
+// 0 publishes the chosen blocks' addresses for the down launch.
+template <int FMT, int NCH, bool TOPK>
+__global__ __launch_bounds__(256) void k_gateup_stream(DecodeArgs a) {
+    constexpr int G = Fmt<FMT>::G;
+    constexpr int DP = kStreamDP;
+    constexpr int NSC = FMT == kFmtNvfp4 ? 2 : 1;  // scale dwords per lane per unit
+    __shared__ const void* blks[kMaxK];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int H = a.H, I = a.I, k = a.k;
+    const int nchunk = H / 32;
+    const uint32_t KB = (uint32_t)H / 2, KS = (uint32_t)H / G;
+    const uint32_t sbase = (uint32_t)3 * I * (H / 2);
+    const int U = k * I;
+    const long long nwg = gridDim.x, b = blockIdx.x;
+    const int wu0 = (int)(U * b / nwg), wu1 = (int)(U * (b + 1) / nwg);
+    const int u0 = wu0 + wave, u1 = wu1;
+    float xs[NCH][32];
+    if constexpr (TOPK) {
+        load_chunk_acts<NCH>(a.x, nchunk, xs);  // in flight during the top-k
+        // slots this workgroup's range touches: 0 .. need-1
+        const int need = wu1 > wu0 ? (wu1 - 1) / I + 1 : 1;
+        const bool publisher = blockIdx.x == gridDim.x - 1;
+        if (threadIdx.x < 64) {
+            int e = -1;
+            float wt = 0.f;
+            topk_select([&](int i) { return a.logits[i]; }, a.E, publisher ? k : need, e, wt);
+            if (lane < k) {
+                const void* bp = valid_block(a, a.expert_ptrs, e);
+                blks[lane] = bp;
+                if (publisher) {
+                    a.idx_out[lane] = e;
+                    a.w_out[lane] = wt;
+                    a.sel[lane] = bp;
+                }
+            }
+        }
+    } else {
+        if ((int)threadIdx.x < k) {
+            const void* bp = valid_block(a, a.expert_ptrs, a.idx[threadIdx.x]);
+            blks[threadIdx.x] = bp;
+            if (blockIdx.x == 0) a.sel[threadIdx.x] = bp;
+        }
+    }
+    lds_barrier();
+    if constexpr (!TOPK) load_chunk_acts<NCH>(a.x, nchunk, xs);  // needed from the first unit on
+
+    const rsrc_t rh = make_rsrc(a.h, (uint32_t)(4 * U));
+    uint4 cw[DP][2][NCH];
+    uint32_t sw[DP][NSC];
+    // loads of unit u into register set d (past the range: out-of-range
+    // offsets, zeros without memory traffic; an invalid expert: a buffer of
+    // 0 bytes)
+    auto issue = [&](int d, int u) {
+        const bool on = u < u1;
+        const int uu = min(on ? u : u0, U - 1);
+        const int slot = uu / I, r = uu % I;
+        const void* blk = uniform_ptr(blks[slot]);
+        const rsrc_t rs = make_rsrc(blk ? blk : (const void*)a.x, blk ? a.block_bytes : 0u);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const uint32_t row = (uint32_t)(h * I + r);
+#pragma unroll
+            for (int m = 0; m < NCH; m++) {
+                const int c = lane + 64 * m;
+                const bool ok = on && c < nchunk;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, sel_u32(ok, row * KB + 16u * c, kOOB), 0, kNT);
+                cw[d][h][m] = uint4{v[0], v[1], v[2], v[3]};
+            }
+        }
+        if constexpr (NSC == 1) {
+            const uint32_t row = (uint32_t)((lane >> 5) * I + r), o = 4u * (lane & 31);
+            sw[d][0] = ld_b32(rs, sel_u32(on && o < KS, sbase + row * KS + o, kOOB));
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t row = (uint32_t)(h * I + r), o = 4u * lane;
+                sw[d][h] = ld_b32(rs, sel_u32(on && o < KS, sbase + row * KS + o, kOOB));
+            }
+        }
+    };
+    // scale bits of chunk c of row h (MXFP4: its byte; NVFP4: its two bytes)
+    auto chunk_scale = [&](const uint32_t (&sc)[NSC], int h, int c) -> uint32_t {
+        if constexpr (NSC == 1) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (h * 32 + (c >> 2)), (int)sc[0]);
+            return v >> (8 * (c & 3));
+        } else {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (c >> 1), (int)sc[h]);
+            return v >> (16 * (c & 1));
+        }
+    };
+    auto compute = [&](int d, int u) {
+        if (u >= u1) {
+            // nothing to compute (uniform), but the set's loads are used here
+            // as on the other path, so that the compiler's waits after this
+            // point stay the same on both
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int m = 0; m < NCH; m++) consume(cw[d][h][m]);
+#pragma unroll
+            for (int i = 0; i < NSC; i++) consume(sw[d][i]);
+            return;
+        }
+        const int slot = u / I, r = u % I;
+        float t[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < NCH; m++) {
+                const int c = min(lane + 64 * m, nchunk - 1);
+                acc = chunk_dot<FMT>(cw[d][h][m], chunk_scale(sw[d], h, c), xs[m], acc);
+            }
+            t[h] = wave_sum(acc);
+        }
+        // one store instruction (lanes other than 0 store to an out-of-range
+        // offset, which is dropped); integer selects, no branch
+        const uint32_t badm = 0u - (uint32_t)(blks[slot] == nullptr);  // all ones: invalid expert -> NaN
+        const uint32_t hv = __float_as_uint(silu_mul(t[0], t[1])) | (badm & 0x7FC00000u);
+        const uint32_t keep = 0u - (uint32_t)(lane == 0);
+        const uint32_t off = 4u * (uint32_t)(slot * I + r);
+        __builtin_amdgcn_raw_buffer_store_b32(hv, rh, (off & keep) | (kOOB & ~keep), 0, 0);
+    };
+    // the empty asm statements keep the units' loads in issue order (the
+    // scheduler would otherwise interleave the sets, and the wait for the
+    // first set would become a wait for all of them)
+#pragma unroll
+    for (int d = 0; d < DP; d++) {
+        issue(d, u0 + 4 * d);
+        asm volatile("" ::: "memory");
+    }
+    for (int ub = u0; ub < u1; ub += 4 * DP) {
+#pragma unroll
+        for (int d = 0; d < DP; d++) {
+            compute(d, ub + 4 * d);
+            issue(d, ub + 4 * (d + DP));
+            asm volatile("" ::: "memory");
+        }
+    }
+}
+
+// down projection + combine, streaming form: workgroup = k waves (wave j:
+// routed slot j) x kStreamRows output rows. Wave j holds its chunks of h[j]
+// in registers and has the loads of all its rows in flight at once. The
+// rows' scale bytes are contiguous in the block: one 16-byte load per lane
+// brings them to the wave's LDS slice (one-byte loads per chunk measured
+// about 1.5x slower for the whole launch), where each lane reads its own.
+// The row sums meet in LDS and thread r forms y[row] = sum_j w[j] *
+// part[j][r] in increasing j (the same order as k_down_combine).
+template <int FMT, int NCH>
+__global__ __launch_bounds__(64 * 8) void k_down_stream(DecodeArgs a) {
+    constexpr int G = Fmt<FMT>::G;
+    constexpr int R = kStreamRows;
+    constexpr int SCB = R * 4096 / G;  // scale bytes of R rows, I <= 4096
+    __shared__ float part[8][R];
+    __shared__ float wsh[8];
+    __shared__ __attribute__((aligned(16))) uint8_t scs[8][SCB];
+    const int tid = threadIdx.x, lane = tid & 63, j = wave_id();
+    const int H = a.H, I = a.I, k = a.k;
+    const int nchunk = I / 32;
+    const uint32_t KB = (uint32_t)I / 2, KS = (uint32_t)I / G;
+    const uint32_t codes0 = (uint32_t)I * H;                                  // down codes [H][I/2]
+    const uint32_t scl0 = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / G;  // down scales [H][I/G]
+    const int n0 = blockIdx.x * R;
+    const void* blk = uniform_ptr(a.sel[j]);
+    const bool bad = blk == nullptr;
+    const rsrc_t rs = make_rsrc(bad ? (const void*)a.x : blk, bad ? 0u : a.block_bytes);
+    uint4 cw[R][NCH];
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const uint32_t row = (uint32_t)(n0 + q);
+#pragma unroll
+        for (int m = 0; m < NCH; m++) {
+            const int c = lane + 64 * m;
+            const auto v =
+                __builtin_amdgcn_raw_buffer_load_b128(rs, sel_u32(c < nchunk, codes0 + row * KB + 16u * c, kOOB), 0, kNT);
+            cw[q][m] = uint4{v[0], v[1], v[2], v[3]};
+        }
+    }
+    // scales of rows n0 .. n0+R-1: R*KS contiguous bytes at a 16-byte
+    // aligned offset (R*KS = I/4 or I/2, a multiple of 16 as I % 64 == 0)
+    constexpr int NSL = (SCB + 1023) / 1024;
+    uint4 sl[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; i++) {
+        const uint32_t o = 16u * (lane + 64 * i);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, sel_u32(o < R * KS, scl0 + n0 * KS + o, kOOB), 0, 0);
+        sl[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+    float hs[NCH][32];
+    load_chunk_acts<NCH>(a.h + (size_t)j * I, nchunk, hs);
+    if (tid < k) wsh[tid] = a.w[tid];
+#pragma unroll
+    for (int i = 0; i < NSL; i++) {
+        const int o = 16 * (lane + 64 * i);
+        if (o < SCB) *reinterpret_cast<uint4*>(&scs[j][o]) = sl[i];
+    }
+    // (this wave's LDS writes and reads stay in order: no barrier needed)
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < NCH; m++) {
+            const int c = min(lane + 64 * m, nchunk - 1);
+            const uint32_t so = (uint32_t)q * KS + (FMT == kFmtNvfp4 ? 2u * c : (uint32_t)c);
+            const uint32_t sc = FMT == kFmtNvfp4 ? *reinterpret_cast<const uint16_t*>(&scs[j][so]) : scs[j][so];
+            acc = chunk_dot<FMT>(cw[q][m], sc, hs[m], acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) part[j][q] = bad ? __uint_as_float(0x7FC00000u) : acc;
+    }
+    __syncthreads();
+    if (tid < R) {
+        float acc = 0.f;
+        for (int jj = 0; jj < k; jj++) acc = fmaf(wsh[jj], part[jj][tid], acc);
+        a.y[n0 + tid] = acc;
+    }
+}
+
+// the stream forms serve layers with no shared expert, k <= 8, I % 64 == 0
+// and at least 32 MB of gate/up codes per token (H, I <= 4096 as for every
+// decode layer)
+static bool use_stream(const DecodeArgs& a) {
+    return !a.has_shared && a.k <= 8 && (size_t)a.k * a.I * a.H >= ((size_t)32 << 20) && a.H % kStreamRows == 0 &&
+           a.I % 64 == 0;
+}
+
+// resident workgroups of a kernel: occupancy per CU times the CU count
+template <class KERNEL>
+static int resident_grid(KERNEL kern, int threads) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess) return 0;
+    return cus * per;
+}
+
+template <int FMT, bool TOPK>
+static hipError_t launch_stream(DecodeArgs& a, hipStream_t s) {
+    const int nch_h = (a.H / 32 + 63) / 64, nch_i = (a.I / 32 + 63) / 64;
+    auto gu = nch_h == 1 ? k_gateup_stream<FMT, 1, TOPK> : k_gateup_stream<FMT, 2, TOPK>;
+    const int grid = resident_grid(gu, 256);
+    if (grid <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gu, dim3(grid), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    auto dn = nch_i == 1 ? k_down_stream<FMT, 1> : k_down_stream<FMT, 2>;
+    hipLaunchKernelGGL(dn, dim3(a.H / kStreamRows), dim3(64 * a.k), 0, s, a);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
 template <int FMT>
 static hipError_t launch_down(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
     const bool sh = a.n_items > a.k;
@@ -645,6 +983,7 @@ static hipError_t launch_down(const DecodePlan& p, DecodeArgs& a, hipStream_t s)
 
 template <int FMT>
 static hipError_t launch_expert(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
+    if (use_stream(a)) return launch_stream<FMT, false>(a, s);
     const int n_gate = a.k * a.gt_r + (a.has_shared ? a.gt_s : 0);
 #define GU(GD, GP) case GD: hipLaunchKernelGGL((k_gateup<FMT, GD, GP>), dim3(n_gate), dim3(256), 0, s, a); break;
     switch (p.gate_D) {
@@ -687,6 +1026,7 @@ static hipError_t launch_layer(const DecodePlan& p, DecodeArgs& a, hipStream_t s
 #undef RS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (use_stream(a)) return launch_stream<FMT, true>(a, s);
     switch (p.gate_D) {
         case 1: e = launch_topk_gateup<FMT, 1, 4>(p, a, s); break;
         case 2: e = launch_topk_gateup<FMT, 2, 4>(p, a, s); break;

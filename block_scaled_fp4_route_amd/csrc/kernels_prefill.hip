@@ -401,7 +401,6 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 // row r at slot r*SPR + (p ^ (r & 7)), which keeps the fragment reads of 8
 // consecutive rows on distinct bank groups. Rows past `rows` load row 0
 // (their sums are never stored).
-constexpr uint32_t kOOB = 0x7FFFFFF0u;  // beyond every buffer here: loads return 0
 
 // 16-byte buffer load straight into LDS: lane l writes lds + 16*l (lds is
 // wave-uniform).

@@ -30,10 +30,14 @@ struct Fmt<kFmtMxfp4> {
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
 
 // UE8M0 byte -> fp32: 2^(u - 127); 255 is NaN; 0 is the fp32 subnormal 2^-127.
+// (selects, no branches: a divergent branch makes LLVM wait for every
+// outstanding load at its join)
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t u) {
     u &= 0xFFu;
-    if (u == 0xFFu) return __uint_as_float(0x7FC00000u);
-    return u ? __uint_as_float(u << 23) : __uint_as_float(0x00400000u);
+    uint32_t b = u << 23;
+    b = u == 0u ? 0x00400000u : b;
+    b = u == 0xFFu ? 0x7FC00000u : b;
+    return __uint_as_float(b);
 }
 
 template <int FMT>
@@ -296,6 +300,11 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// Buffer offset beyond every buffer the kernels address: loads from it
+// return 0 without touching memory (used for loads that must be issued but
+// have nothing to read, so that every path issues the same loads).
+constexpr uint32_t kOOB = 0x7FFFFFF0u;
 
 // The wave's index in its workgroup, as a value the compiler knows is uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

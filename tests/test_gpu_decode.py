@@ -148,6 +148,10 @@ def test_decode_deterministic_reruns(m, orc):
     ("nvfp4", 3072, 1040, 6, 3),   # down rows of 130 dwords: ragged lane coverage
     ("nvfp4", 512, 256, 40, 32),   # k = 32: sixteen routed pairs fill the down workgroup
     ("mxfp4", 512, 320, 9, 7),     # odd k: the last down pair holds one item
+    # layers of >= 32 MB of gate/up codes without a shared expert take the
+    # streaming kernels: one 1 KB chunk per lane and row, 1.5 chunks, 2 chunks
+    ("mxfp4", 2048, 2048, 10, 8),
+    ("nvfp4", 3072, 1536, 9, 8),
 ])
 def test_decode_edge_shapes(m, orc, fmt, H, I, E, k):
     wl = sg.Workload("edge", 90, H, I, E, k, fmt, 1, 1, False, "router", 0.0,
@@ -241,16 +245,18 @@ def test_one_workspace_across_layers_and_calls(m, orc):
         assert rel_err(y.cpu().numpy(), ref) <= TOL
 
 
-def test_expert_index_out_of_range_poisons_output(m):
+@pytest.mark.parametrize("name", ["qwen_layer_decode", "deepseek_decode"])
+def test_expert_index_out_of_range_poisons_output(m, name):
     """An expert index outside [0, E) is not dereferenced: the output turns
-    NaN instead (the host cannot check device-resident indices)."""
-    wl = sg.get("qwen_layer_decode")
+    NaN instead (the host cannot check device-resident indices). The
+    DeepSeek shape runs the streaming kernels."""
+    wl = sg.get(name)
     E = 12
     d = m.desc(wl.H, wl.I, E, wl.k, wl.fmt)
     blocks = layer_blocks(wl, 0, E=E)
     ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
     x = sg.activations(wl, 0, 0, T=1, device="cuda").view(-1)
-    idx = torch.tensor([0, 1, 2, 3, 4, 5, 6, 7, 8, 15], dtype=torch.int32, device="cuda")
+    idx = torch.tensor(list(range(wl.k - 1)) + [15], dtype=torch.int32, device="cuda")
     w = torch.full((wl.k,), 0.1, dtype=torch.float32, device="cuda")
     y = torch.empty(wl.H, dtype=torch.float32, device="cuda")
     m.moe_expert_decode(d, x, m.expert_ptr_table(blocks), idx, w, None, y, ws)
