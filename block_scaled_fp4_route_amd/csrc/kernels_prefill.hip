@@ -108,62 +108,103 @@ __device__ __forceinline__ int wave_sum_int(int v) {
     return v;
 }
 
-// grid E, 1024 threads per expert e, two passes over idx and no dependency
-// between workgroups: pass 1 counts lt = #{a : idx[a] < e} (= off[e], the
-// exclusive prefix sum of the counts) and eq = #{a : idx[a] == e}; pass 2
-// writes perm[off[e] + r] = the r-th assignment (in increasing a) routed to e
-// and pos[a] = its grouped position. Assignments whose expert index lies
-// outside [0, E) match no workgroup; workgroup e sets pos = -1 for those in
-// its slice of the array (a valid entry is only ever written by its expert's
-// workgroup, so the writes never collide).
+// grid ceil(E/4), 1024 threads; workgroup b handles the experts e0 = 4b ..
+// e0+3 (those below E) and no workgroup depends on another. Wave w owns the
+// contiguous slice [n*w/16, n*(w+1)/16) of the assignments a = t*k + j; its
+// lane l takes a = lo + 64*i + l, so the order (i, l) is increasing a. Each
+// pass issues all of a wave's loads of up to kGroupPer entries per lane
+// together (one memory latency per pass for n <= 16*64*kGroupPer). Pass 1
+// counts lt = #{a : idx[a] < e0} (summed over the workgroup: off[e0], the
+// exclusive prefix sum of the counts) and eq[d] = #{a : idx[a] == e0 + d}
+// per wave; one barrier gives every wave the matches of the waves before it.
+// Pass 2 writes perm[off[e] + r] = the r-th assignment (in increasing a)
+// routed to e and pos[a] = its grouped position. Assignments whose expert
+// index lies outside [0, E) match no expert; workgroup b sets pos = -1 for
+// those in its slice [n*b/G, n*(b+1)/G) of the array (G workgroups; a valid
+// entry is only ever written by its expert's workgroup, so the writes never
+// collide).
+constexpr int kGroupPer = 24;
+constexpr int kGroupExperts = 4;
+
 __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ idx, int n, int E,
                                                          int* __restrict__ count, int* __restrict__ off,
                                                          int* __restrict__ perm, int* __restrict__ pos) {
-    __shared__ int red[2][kGroupThreads / 64];
-    __shared__ int wtot[kGroupThreads / 64];
-    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int NW = kGroupThreads / 64;
-    int lt = 0, eq = 0;
-    for (int a = tid; a < n; a += kGroupThreads) {
-        const int v = idx[a];
-        lt += (unsigned)v < (unsigned)e;
-        eq += v == e;
+    constexpr int NW = kGroupThreads / 64, ND = kGroupExperts;
+    __shared__ int red_lt[NW], red_eq[ND][NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e0 = ND * blockIdx.x;
+    const int lo = (int)((long long)n * wave / NW), hi = (int)((long long)n * (wave + 1) / NW);
+    int lt = 0, eq[ND] = {};
+    for (int a0 = lo; a0 < hi; a0 += 64 * kGroupPer) {
+        int v[kGroupPer];
+#pragma unroll
+        for (int i = 0; i < kGroupPer; i++) {
+            const int a = a0 + 64 * i + lane;
+            v[i] = a < hi ? idx[a] : E;
+        }
+#pragma unroll
+        for (int i = 0; i < kGroupPer; i++) {
+            lt += (unsigned)v[i] < (unsigned)e0;
+#pragma unroll
+            for (int d = 0; d < ND; d++) eq[d] += v[i] == e0 + d && e0 + d < E;
+        }
     }
     lt = wave_sum_int(lt);
-    eq = wave_sum_int(eq);
-    if (lane == 0) { red[0][wave] = lt; red[1][wave] = eq; }
-    __syncthreads();
-    int base = 0, cnt = 0;
-    for (int i = 0; i < NW; i++) { base += red[0][i]; cnt += red[1][i]; }
-    if (tid == 0) {
-        off[e] = base;
-        count[e] = cnt;
-        if (e == E - 1) off[E] = base + cnt;
+#pragma unroll
+    for (int d = 0; d < ND; d++) eq[d] = wave_sum_int(eq[d]);
+    if (lane == 0) {
+        red_lt[wave] = lt;
+#pragma unroll
+        for (int d = 0; d < ND; d++) red_eq[d][wave] = eq[d];
     }
-    const int lo = (int)((long long)n * e / E), hi = (int)((long long)n * (e + 1) / E);
-    for (int a = lo + tid; a < hi; a += kGroupThreads)
-        if ((unsigned)idx[a] >= (unsigned)E) pos[a] = -1;
-    const unsigned long long below = (1ull << lane) - 1ull;
-    int running = base;
-    for (int a0 = 0; a0 < n; a0 += kGroupThreads) {
-        const int a = a0 + tid;
-        const bool match = a < n && idx[a] == e;
-        const unsigned long long m = __ballot(match);
-        if (lane == 0) wtot[wave] = __popcll(m);
-        __syncthreads();
-        int wave_pre = 0, total = 0;
+    __syncthreads();
+    int base = 0, mine = 0;
+    for (int i = 0; i < NW; i++) base += red_lt[i];
+    int running[ND];
+#pragma unroll
+    for (int d = 0; d < ND; d++) {
+        int cnt = 0, pre = 0;
         for (int i = 0; i < NW; i++) {
-            const int t = wtot[i];
-            wave_pre += i < wave ? t : 0;
-            total += t;
+            cnt += red_eq[d][i];
+            pre += i < wave ? red_eq[d][i] : 0;
         }
-        if (match) {
-            const int p = running + wave_pre + __popcll(m & below);
-            perm[p] = a;
-            pos[a] = p;
+        running[d] = base + pre;
+        mine += red_eq[d][wave];
+        if (tid == 0 && e0 + d < E) {
+            off[e0 + d] = base;
+            count[e0 + d] = cnt;
+            if (e0 + d == E - 1) off[E] = base + cnt;
         }
-        running += total;
-        __syncthreads();
+        base += cnt;
+    }
+    const int G = gridDim.x;
+    const int slo = (int)((long long)n * blockIdx.x / G), shi = (int)((long long)n * (blockIdx.x + 1) / G);
+    for (int a = slo + tid; a < shi; a += kGroupThreads)
+        if ((unsigned)idx[a] >= (unsigned)E) pos[a] = -1;
+    if (mine == 0) return;  // wave-uniform: this wave's slice holds no match
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int a0 = lo; a0 < hi; a0 += 64 * kGroupPer) {
+        int v[kGroupPer];
+#pragma unroll
+        for (int i = 0; i < kGroupPer; i++) {
+            const int a = a0 + 64 * i + lane;
+            v[i] = a < hi ? idx[a] : E;
+        }
+#pragma unroll
+        for (int i = 0; i < kGroupPer; i++) {
+            const int a = a0 + 64 * i + lane;
+#pragma unroll
+            for (int d = 0; d < ND; d++) {
+                const bool match = v[i] == e0 + d && e0 + d < E;
+                const unsigned long long m = __ballot(match);
+                if (match) {
+                    const int p = running[d] + __popcll(m & below);
+                    perm[p] = a;
+                    pos[a] = p;
+                }
+                running[d] += __popcll(m);
+            }
+        }
     }
 }
 
@@ -188,18 +229,44 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
                                                              int max_slots, const int* __restrict__ off,
                                                              const void* const* __restrict__ expert_ptrs) {
     __shared__ int cnt[kMaxE];
+    __shared__ uint4 key4[kMaxE / 4];
+    __shared__ int rank[kMaxE];
     __shared__ int nt_sorted[kMaxE];
     __shared__ int ex_sorted[kMaxE];
     __shared__ int start[kGroupThreads + 1];
+    unsigned* key = reinterpret_cast<unsigned*>(key4);
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += kGroupThreads) cnt[e] = count[e];
+    const int E4 = (E + 3) / 4;
+    // key: larger count first, then lower index (counts clamped to 22 bits,
+    // which only coarsens the order of the tile list)
+    for (int e = tid; e < 4 * E4; e += kGroupThreads) {
+        int c = 0;
+        if (e < E) {
+            c = count[e];
+            cnt[e] = c;
+            rank[e] = 0;
+        }
+        key[e] = e < E ? ((0x3FFFFFu - (unsigned)min(c, 0x3FFFFF)) << 10) | (unsigned)e : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    // rank[e] = #{j : key[j] < key[e]}, the comparisons split into P parts
+    // over all threads (the loop is bound by VALU issue)
+    const int P = max(1, kGroupThreads / E);
+    for (int u = tid; u < E * P; u += kGroupThreads) {
+        const int e = u % E, part = u / E;
+        const unsigned ke = key[e];
+        int r = 0;
+#pragma unroll 4
+        for (int j4 = part * E4 / P; j4 < (part + 1) * E4 / P; j4++) {
+            const uint4 q = key4[j4];
+            r += (q.x < ke) + (q.y < ke) + (q.z < ke) + (q.w < ke);
+        }
+        atomicAdd(&rank[e], r);
+    }
     __syncthreads();
     for (int e = tid; e < E; e += kGroupThreads) {
-        const int c = cnt[e];
-        int rank = 0;
-        for (int j = 0; j < E; j++) rank += (cnt[j] > c) || (cnt[j] == c && j < e);
-        ex_sorted[rank] = e;
-        nt_sorted[rank] = (c + BM - 1) / BM;
+        ex_sorted[rank[e]] = e;
+        nt_sorted[rank[e]] = (cnt[e] + BM - 1) / BM;
     }
     __syncthreads();
     // inclusive scan of nt_sorted (Hillis-Steele over kGroupThreads >= E entries)
@@ -214,28 +281,32 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
     if (tid == 0) start[0] = 0;
     if (tid == kGroupThreads - 1) ntiles[0] = v;
     __syncthreads();
-    for (int r = tid; r < E; r += kGroupThreads) {
-        const int e = ex_sorted[r];
-        for (int m = 0; m < nt_sorted[r]; m++) {
-            tile_e[start[r] + m] = e;
-            tile_m[start[r] + m] = m * BM;
-            if (rec) {
-                TileRec t;
-                t.blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
-                t.base = off[e] + m * BM;
-                t.rows = min(BM, cnt[e] - m * BM);
-                rec[start[r] + m] = t;
-            }
-        }
-    }
-    if (rec) {
-        const int used = start[kGroupThreads];
-        for (int i = used + tid; i < max_slots; i += kGroupThreads) {
+    // one thread per tile slot: its rank r is the last with start[r] <= slot
+    const int used = start[E];
+    const int slots = rec ? max_slots : used;
+    for (int sl = tid; sl < slots; sl += kGroupThreads) {
+        if (sl >= used) {
             TileRec t;
             t.blk = nullptr;
             t.base = 0;
             t.rows = 0;
-            rec[i] = t;
+            rec[sl] = t;
+            continue;
+        }
+        int lo = 0, hi = E - 1;  // start[lo] <= sl < start[hi + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (start[mid] <= sl) lo = mid; else hi = mid - 1;
+        }
+        const int e = ex_sorted[lo], m = sl - start[lo];
+        tile_e[sl] = e;
+        tile_m[sl] = m * BM;
+        if (rec) {
+            TileRec t;
+            t.blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
+            t.base = off[e] + m * BM;
+            t.rows = min(BM, cnt[e] - m * BM);
+            rec[sl] = t;
         }
     }
 }
@@ -399,8 +470,8 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 // loads exactly, and the explicit waits before each barrier cover the LDS
 // loads it cannot see. A rows are stored without padding, 16-byte piece p of
 // row r at slot r*SPR + (p ^ (r & 7)), which keeps the fragment reads of 8
-// consecutive rows on distinct bank groups. Rows past `rows` load row 0
-// (their sums are never stored).
+// consecutive rows on distinct bank groups. Rows past `rows` take the
+// out-of-range offset (zeros, no memory traffic; their sums are never stored).
 
 // 16-byte buffer load straight into LDS: lane l writes lds + 16*l (lds is
 // wave-uniform).
@@ -429,9 +500,11 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
     const rsrc_t rb = make_rsrc(blk, block_bytes);
     // this lane's A loads: LDS slot P = (wave*NAI + i)*64 + lane
     uint32_t aoff[NAI];
+    bool aon[NAI];
 #pragma unroll
     for (int i = 0; i < NAI; i++) {
         const int P = (wave * NAI + i) * 64 + lane, r = P / SPR, q = P % SPR;
+        aon[i] = r < rows;
         aoff[i] = 2u * (uint32_t)(a_row(r < rows ? r : 0) + 8 * (q ^ (r & 7)));
     }
     uint32_t boff[4], soff[4];
@@ -447,7 +520,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
         for (int i = 0; i < NAI; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (__attribute__((address_space(3))) void*)(lds + (size_t)buf * 64 * BK + (size_t)(wave * NAI + i) * 64 * 8),
-                16, on ? aoff[i] + 2u * ch * BK : kOOB, 0, 0, 0);
+                16, on && aon[i] ? aoff[i] + 2u * ch * BK : kOOB, 0, 0, 0);
     };
     auto load_b = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4]) {
         const bool on = ch < nchunks;
@@ -948,7 +1021,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     int* perm = dbg && dbg->perm ? dbg->perm : L.perm;
     int* off = dbg && dbg->off ? dbg->off : L.off;
 
-    hipLaunchKernelGGL(k_group, dim3(E), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
+    hipLaunchKernelGGL(k_group, dim3((E + kGroupExperts - 1) / kGroupExperts), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
     LAUNCH_CHECK();
     TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
     hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, L.tile_e, L.tile_m, L.ntiles,

@@ -204,6 +204,12 @@ def test_prefill_mxfp4_T_sweep(m, orc, T):
     full_check(m, orc, wl_small("mxfp4", 512, 64, 8, 2, T), T)
 
 
+def test_prefill_grouping_many_assignments(m, orc):
+    """28,000 assignments: the grouping kernel's waves take their slices in
+    more than one round of loads; perm/off stay bit-exact."""
+    full_check(m, orc, wl_small("nvfp4", 512, 128, 9, 4, 7000), 7000, sample=[0, 1, 3500, 6999])
+
+
 def test_prefill_nvfp4_qwen_shape_small_E(m, orc):
     """Qwen expert shape (H 2560, I 640, top-10) with 24 experts, 40 tokens,
     some experts unused, Zipf skew."""
@@ -258,6 +264,7 @@ def test_prefill_invalid_expert_index_gives_nan_row(m):
     x = sg.activations(wl, 0, 0, T=5, device="cuda")
     idx, w = sg.routing(wl, T=5)
     idx[2, 1] = 99
+    idx[4, 0] = wl.E  # just past the last expert
     g = run_gpu(m, wl, blocks, x, idx.cuda(), w.cuda(), False, dbg=False)
-    assert np.isnan(g["out"][2]).all()
-    assert np.isfinite(np.delete(g["out"], 2, axis=0)).all()
+    assert np.isnan(g["out"][[2, 4]]).all()
+    assert np.isfinite(np.delete(g["out"], [2, 4], axis=0)).all()
