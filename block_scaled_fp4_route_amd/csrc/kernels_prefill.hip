@@ -483,7 +483,7 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off)
 // code that uses a or b after it cannot be scheduled before it.
 __device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
-template <int BK, class AROW>
+template <int BK, int RB, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
                                          uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
@@ -561,24 +561,26 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
             const __bf16* At = lds + (size_t)(ch & 1) * 64 * BK;
 #pragma unroll
             for (int s = 0; s < NS; s++) {
-                bf16x8 bf[4];
+                // the A fragments of all row blocks first (the 64-row tile is
+                // always allocated), so their LDS latency hides behind the decode
+                const int p = (QK / 8) * g + s;  // 16-byte piece of the fragment
+                bf16x8 af[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; rb++) {
+                    const int r = 16 * rb + m16;
+                    af[rb] = *reinterpret_cast<const bf16x8*>(At + (r * SPR + (p ^ (r & 7))) * 8);
+                }
+                // no branches inside a chunk: the MFMAs of column block cb can
+                // issue between the decode instructions of block cb+1
 #pragma unroll
                 for (int cb = 0; cb < 4; cb++) {
                     const uint4 q = bc[cb][s / 4];
                     const uint32_t d = (s & 3) == 0 ? q.x : ((s & 3) == 1 ? q.y : ((s & 3) == 2 ? q.z : q.w));
                     const float sv = e4m3_to_f32((sc[cb] >> (8 * (s / 2))) & 0xFFu);
-                    bf[cb] = dequant8_bf16(d, sv);
-                }
-                const int p = (QK / 8) * g + s;  // 16-byte piece of the fragment
+                    const bf16x8 bf = dequant8_bf16(d, sv);
 #pragma unroll
-                for (int rb = 0; rb < 4; rb++) {
-                    if (16 * rb < rows) {  // uniform: skip padding row blocks of a short tile
-                        const int r = 16 * rb + m16;
-                        const bf16x8 af = *reinterpret_cast<const bf16x8*>(At + (r * SPR + (p ^ (r & 7))) * 8);
-#pragma unroll
-                        for (int cb = 0; cb < 4; cb++)
-                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[cb], acc[rb][cb], 0, 0, 0);
-                    }
+                    for (int rb = 0; rb < RB; rb++)
+                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rb], bf, acc[rb][cb], 0, 0, 0);
                 }
             }
         }
@@ -617,7 +619,13 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<kBKGate>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
+    // the K loop is specialised on the tile's row blocks (wave-uniform)
+    if (rows <= 16)
+        nv_kloop<kBKGate, 1>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
+    else if (rows <= 32)
+        nv_kloop<kBKGate, 2>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
+    else
+        nv_kloop<kBKGate, 4>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
     const int g = lane >> 4;
@@ -664,7 +672,12 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<kBKDown>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
+    if (rows <= 16)
+        nv_kloop<kBKDown, 1>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
+    else if (rows <= 32)
+        nv_kloop<kBKDown, 2>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
+    else
+        nv_kloop<kBKDown, 4>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
