@@ -555,6 +555,85 @@ int orc_quant_mxfp4_rows(int T, int n, const float *x, uint8_t *packed, uint8_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 activation quantiser with a UE8M0 scale per block                     */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_SCALE_FLOOR 0 /* [OCP-MX]: X = floor(log2 amax) - 8 (may saturate) */
+#define ORC_SCALE_CEIL  1 /* smallest X with amax <= 448 * 2^X (never saturates) */
+
+/* E4M3 code of the real value t: the nearest of the finite E4M3 values
+ * (codes 0..126 and their negatives), found by searching the whole grid;
+ * ties go to the code with an even mantissa bit; magnitudes above 448
+ * saturate to 448 (code 0x7E). Negative values that round to zero keep the
+ * sign (code 0x80). */
+static int e4m3_round(double t)
+{
+    double a = fabs(t);
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 127; c++) {
+        double d = fabs(a - orc_e4m3(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            bestd = d;
+            best = c;
+        }
+    }
+    if (a > 448.0)
+        best = 0x7E;
+    return (t < 0 || (t == 0 && signbit(t))) ? (best | 0x80) : best;
+}
+
+/* One block of n values to E4M3 codes with a shared UE8M0 scale ([D] "Three
+ * bugs", item 2: DeepSeek's activation quantiser writes FP8 with ue8m0
+ * scales; [OCP-MX] MXFP8 is the same format with blocks of 32). The shared
+ * exponent X is clamped to [-127, 127] and stored as the byte X + 127; the
+ * codes are e4m3_round(v / 2^X). An all-zero block gets scale byte 0 and
+ * zero codes. */
+void orc_fp8_quant(const double *v, int n, int rule, uint8_t *codes, uint8_t *scale_byte)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; i++)
+        if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    if (amax == 0.0) {
+        *scale_byte = 0;
+        for (int i = 0; i < n; i++)
+            codes[i] = signbit(v[i]) ? 0x80 : 0;
+        return;
+    }
+    int e;
+    frexp(amax, &e);                      /* amax in [2^(e-1), 2^e) */
+    int X = (e - 1) - 8;                  /* 8 = largest exponent of E4M3 */
+    if (rule == ORC_SCALE_CEIL) {
+        X = (e - 1) - 9;
+        while (amax > ldexp(448.0, X))
+            X++;
+    }
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    *scale_byte = (uint8_t)(X + 127);
+    for (int i = 0; i < n; i++)
+        codes[i] = (uint8_t)e4m3_round(ldexp(v[i], -X));
+}
+
+/* Rows of n values, blocks of `block` consecutive values: codes [T][n],
+ * scales [T][n/block]. */
+int orc_quant_fp8_rows(int T, int n, int block, int rule, const float *x, uint8_t *codes, uint8_t *scales)
+{
+    if (block <= 0 || block > 1024 || n % block)
+        return -1;
+    double v[1024];
+    for (int t = 0; t < T; t++)
+        for (int b = 0; b < n / block; b++) {
+            for (int i = 0; i < block; i++)
+                v[i] = x[(int64_t)t * n + (int64_t)b * block + i];
+            orc_fp8_quant(v, block, rule, codes + (int64_t)t * n + (int64_t)b * block,
+                          &scales[(int64_t)t * (n / block) + b]);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Grouping of (token, slot) assignments by expert                           */
 /* ------------------------------------------------------------------------ */
 

@@ -58,6 +58,8 @@ def lib():
         L.orc_quant_bf16_rows.restype = None; L.orc_quant_bf16_rows.argtypes = [I32, I32, P, P]
         L.orc_quant_mxfp4_rows.restype = I32; L.orc_quant_mxfp4_rows.argtypes = [I32, I32, P, P, P]
         L.orc_group.restype = I32; L.orc_group.argtypes = [I32, I32, I32, P, P, P, P]
+        L.orc_fp8_quant.restype = None; L.orc_fp8_quant.argtypes = [P, I32, I32, P, P]
+        L.orc_quant_fp8_rows.restype = I32; L.orc_quant_fp8_rows.argtypes = [I32, I32, I32, I32, P, P, P]
         L.orc_moe_prefill.restype = I32
         L.orc_moe_prefill.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, I32, I32, P, P, P, I32]
         _lib = L
@@ -195,6 +197,27 @@ def quant_mxfp4_rows(x):
     if lib().orc_quant_mxfp4_rows(T, n, _p(x2), _p(packed), _p(sc)):
         raise ValueError("row length must be a multiple of 32")
     return packed, sc
+
+
+SCALE_FLOOR, SCALE_CEIL = 0, 1
+
+
+def fp8_quant(v, rule=SCALE_FLOOR):
+    """One block to E4M3 codes and its UE8M0 scale byte."""
+    v = _c(v, np.float64)
+    codes = np.empty(v.size, np.uint8); sb = np.zeros(1, np.uint8)
+    lib().orc_fp8_quant(_p(v), v.size, int(rule), _p(codes), _p(sb))
+    return codes, int(sb[0])
+
+
+def quant_fp8_rows(x, block=32, rule=SCALE_FLOOR):
+    """Rows of fp32 values to E4M3 codes [T][n] and UE8M0 scales [T][n/block]."""
+    x = _c(x, np.float32); x2 = x.reshape(x.shape[0], -1) if x.ndim > 1 else x.reshape(1, -1)
+    T, n = x2.shape
+    codes = np.empty((T, n), np.uint8); sc = np.empty((T, n // block), np.uint8)
+    if lib().orc_quant_fp8_rows(T, n, int(block), int(rule), _p(x2), _p(codes), _p(sc)):
+        raise ValueError("row length must be a multiple of the block")
+    return codes, sc
 
 
 def group(idx, E):
