@@ -633,6 +633,19 @@ int orc_quant_fp8_rows(int T, int n, int block, int rule, const float *x, uint8_
     return 0;
 }
 
+/* Row-scaled FP8 matrix-vector product ([Q] "The engine", item 4; [Q] "Why
+ * this model, of all models": dense matrices in FP8 with one scale per
+ * row): y[r] = s[r] * sum_c e4m3(W[r][c]) * x[c], in fp64. */
+void orc_gemv_fp8(int rows, int cols, const uint8_t *W, const float *s, const float *x, double *y)
+{
+    for (int r = 0; r < rows; r++) {
+        double acc = 0.0;
+        for (int c = 0; c < cols; c++)
+            acc += orc_e4m3(W[(int64_t)r * cols + c]) * (double)x[c];
+        y[r] = (double)s[r] * acc;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Grouping of (token, slot) assignments by expert                           */
 /* ------------------------------------------------------------------------ */

@@ -60,6 +60,7 @@ def lib():
         L.orc_group.restype = I32; L.orc_group.argtypes = [I32, I32, I32, P, P, P, P]
         L.orc_fp8_quant.restype = None; L.orc_fp8_quant.argtypes = [P, I32, I32, P, P]
         L.orc_quant_fp8_rows.restype = I32; L.orc_quant_fp8_rows.argtypes = [I32, I32, I32, I32, P, P, P]
+        L.orc_gemv_fp8.restype = None; L.orc_gemv_fp8.argtypes = [I32, I32, P, P, P, P]
         L.orc_moe_prefill.restype = I32
         L.orc_moe_prefill.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, I32, I32, P, P, P, I32]
         _lib = L
@@ -218,6 +219,15 @@ def quant_fp8_rows(x, block=32, rule=SCALE_FLOOR):
     if lib().orc_quant_fp8_rows(T, n, int(block), int(rule), _p(x2), _p(codes), _p(sc)):
         raise ValueError("row length must be a multiple of the block")
     return codes, sc
+
+
+def gemv_fp8(W, s, x):
+    """y = s * (e4m3(W) x) in fp64; W uint8 [rows, cols], s fp32 [rows], x fp32 [cols]."""
+    W = _c(W, np.uint8); s = _c(s, np.float32); x = _c(x, np.float32)
+    rows, cols = W.shape
+    y = np.empty(rows, np.float64)
+    lib().orc_gemv_fp8(rows, cols, _p(W), _p(s), _p(x), _p(y))
+    return y
 
 
 def group(idx, E):

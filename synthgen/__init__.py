@@ -208,9 +208,39 @@ def decode_routing(wl: Workload, layer: int, step: int = 0, device="cpu") -> tup
     return idx.view(wl.k), w.view(wl.k)
 
 
+# ---------------------------------------------------------------------------
+# FP8 inputs (stream namespace 90: the activation quantiser, 91: the
+# row-scaled GEMV)
+F8_ACT, F8_CODES, F8_SCALES, F8_X = 90, 91, 92, 93
+
+
+def fp8_activations(rows: int, cols: int, seed_id: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [rows, cols] N(0, 1) rows for the FP8 activation quantiser."""
+    return normal(stream_key(F8_ACT, seed_id, rows, cols), rows * cols, 1.0, device).view(rows, cols)
+
+
+def fp8_matrix(rows: int, cols: int, seed_id: int = 0, device="cpu") -> torch.Tensor:
+    """uint8 [rows, cols] codes uniform over the 254 finite E4M3 bytes
+    (0x7F and 0xFF, the two NaN codes, are skipped)."""
+    u = uniform_codes(stream_key(F8_CODES, seed_id, rows, cols), rows * cols, 0, 253, device).to(torch.int32)
+    return (u + (u >= 127).to(torch.int32)).to(torch.uint8).view(rows, cols)
+
+
+def fp8_row_scales(rows: int, seed_id: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [rows] positive row scales 2^-8 * (1 + u), u uniform in [0, 1)."""
+    u = uniform01(stream_key(F8_SCALES, seed_id, rows), rows, device)
+    return ((1.0 + u) * 2.0 ** -8).to(torch.float32)
+
+
+def fp8_vector(cols: int, seed_id: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [cols] N(0, 1) input vector of the GEMV."""
+    return normal(stream_key(F8_X, seed_id, cols), cols, 1.0, device)
+
+
 __all__ = [
     "SEED", "GAMMA", "mix64", "mix64_int", "stream_key", "words", "uniform_bytes",
     "uniform_codes", "uniform01", "normal", "WORKLOADS", "Workload", "get",
     "block_region_sizes", "expert_blocks", "fill_layer_blocks", "router_weights",
-    "shared_expert", "activations", "routing", "decode_routing",
+    "shared_expert", "activations", "routing", "decode_routing", "fp8_activations", "fp8_matrix",
+    "fp8_row_scales", "fp8_vector",
 ]

@@ -106,3 +106,42 @@ def test_rows_layout(orc):
             assert (codes[t, 32 * b:32 * b + 32] == c).all() and sc[t, b] == sb
     with pytest.raises(ValueError):
         orc.quant_fp8_rows(x, block=64)
+
+
+# ---------------------------------------------------------------------------
+# row-scaled FP8 GEMV
+
+
+def test_gemv_fp8_integer_exact(orc):
+    """Codes of small integers, integer x and unit scales: every partial sum
+    is an exact integer, so the result equals numpy's integer product."""
+    rng = np.random.default_rng(11)
+    ints = np.array([0, 1, 2, 3, 4, -1, -2, -3, -4, 6, -6, 8], np.float32)
+    codes = torch.tensor(ints).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sel = rng.integers(0, len(ints), (7, 96))
+    W = codes[sel]
+    x = rng.integers(-5, 6, 96).astype(np.float32)
+    y = orc.gemv_fp8(W, np.ones(7, np.float32), x)
+    ref = ints[sel].astype(np.int64) @ x.astype(np.int64)
+    assert (y == ref).all()
+
+
+def test_gemv_fp8_matches_torch_decode_and_numpy(orc):
+    """Against torch's float8_e4m3fn decoder and a float64 numpy product."""
+    import synthgen as sg
+    W = sg.fp8_matrix(33, 512, 1).numpy()
+    s = sg.fp8_row_scales(33, 1).numpy()
+    x = sg.fp8_vector(512, 1).numpy()
+    Wf = torch.from_numpy(W).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = s.astype(np.float64) * (Wf @ x.astype(np.float64))
+    y = orc.gemv_fp8(W, s, x)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+    # the row scale belongs to its own row: a shift by one row is far off
+    assert np.abs(np.roll(s, 1) * (Wf @ x) - y).max() > 0.1 * np.abs(y).max()
+
+
+def test_fp8_matrix_generator_skips_nan_codes():
+    import synthgen as sg
+    W = sg.fp8_matrix(64, 1024, 3).numpy()
+    assert not np.isin(W, [0x7F, 0xFF]).any()
+    assert len(np.unique(W)) == 254
