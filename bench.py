@@ -328,6 +328,98 @@ def run_prefill(args, m, sg, torch):
     return res
 
 
+FP8_WORKLOADS = {
+    # rows = tokens of the DeepSeek-shaped hidden size; the pages check the
+    # quantiser at 1, 17, 300 and 1024 rows ([D] "Three bugs", item 2)
+    "fp8_act_quant": {"rows": 1024, "cols": 4096, "block": 32, "rule": "floor"},
+    # a dense FP8 matrix of the Qwen-shaped hidden size (the pages give no
+    # shape for their FP8 matrices; 8192 x 2560 stands in for them)
+    "fp8_gemv": {"rows": 8192, "cols": 2560},
+}
+
+
+def run_fp8(args, m, sg, torch):
+    """The FP8 kernels beside the MoE path: K calls captured in a HIP graph,
+    rotating over input replicas that together exceed the 256 MB MALL, so
+    every call reads HBM."""
+    cfg = dict(FP8_WORKLOADS[args.workload])
+    K, W = args.steps, args.warmup
+    rows, cols = cfg["rows"], cfg["cols"]
+    if args.workload == "fp8_act_quant":
+        block, rule = cfg["block"], (m.MOE_SCALE_FLOOR if cfg["rule"] == "floor" else m.MOE_SCALE_CEIL)
+        in_bytes = rows * cols * 4
+        nrep = max(2, -(-384 * 2**20 // in_bytes))
+        xs = [sg.fp8_activations(rows, cols, r, device="cuda") for r in range(nrep)]
+        codes = [torch.empty((rows, cols), dtype=torch.uint8, device="cuda") for _ in range(nrep)]
+        scales = [torch.empty((rows, cols // block), dtype=torch.uint8, device="cuda") for _ in range(nrep)]
+
+        def call(i):
+            j = i % nrep
+            m.moe_act_quant_fp8(xs[j], rows, cols, block, rule, codes[j], scales[j])
+        nbytes = in_bytes + rows * cols + rows * cols // block
+        kernel, unit_name = "k_act_quant_fp8", "rows/s"
+    else:
+        mat_bytes = rows * cols
+        nrep = max(2, -(-384 * 2**20 // mat_bytes))
+        Ws = [sg.fp8_matrix(rows, cols, r, device="cuda") for r in range(nrep)]
+        ss = [sg.fp8_row_scales(rows, r, device="cuda") for r in range(nrep)]
+        x = sg.fp8_vector(cols, 0, device="cuda")
+        ys = [torch.empty(rows, device="cuda") for _ in range(nrep)]
+
+        def call(i):
+            j = i % nrep
+            m.moe_gemv_fp8(Ws[j], ss[j], x, rows, cols, ys[j])
+        nbytes = mat_bytes + 8 * rows + 4 * cols
+        kernel, unit_name = "k_gemv_fp8", "GEMV/s"
+    for i in range(W):
+        call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(K):
+                call(i)
+    torch.cuda.current_stream().wait_stream(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / K
+    gbps = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC, "value": round((rows if args.workload == "fp8_act_quant" else 1) / (us * 1e-6), 1),
+        "unit": unit_name, "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 in, e4m3 out" if args.workload == "fp8_act_quant" else "e4m3 weights, f32 accumulate",
+        "data": "synthetic (seeded SplitMix64)",
+        "config": {"workload": args.workload, **cfg, "replicas": nrep, "launch": "hip_graph",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": TRAFFIC.get(args.workload),
+                     "bytes_per_launch": nbytes, "avg_us": round(us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        t0 = time.perf_counter()
+        if args.workload == "fp8_act_quant":
+            n = 64
+            O.quant_fp8_rows(xs[0][:n].cpu().numpy(), block=block, rule=rule)
+            el = time.perf_counter() - t0
+            res["cpu_baseline"] = {"value": n / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                   "sample": f"{n} of {rows} rows, {cols} values each"}
+        else:
+            O.gemv_fp8(Ws[0].cpu().numpy(), ss[0].cpu().numpy(), x.cpu().numpy())
+            el = time.perf_counter() - t0
+            res["cpu_baseline"] = {"value": 1.0 / el, "unit": "GEMV/s", "cores": 1, "kind": "oracle",
+                                   "sample": f"one full {rows} x {cols} product (fp64)"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,8 +451,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": 1 << 30, "copies": 4}), flush=True)
         return
-    wl = sg.get(args.workload)
-    res = run_prefill(args, m, sg, torch) if wl.is_prefill else run_decode(args, m, sg, torch)
+    if args.workload in FP8_WORKLOADS:
+        res = run_fp8(args, m, sg, torch)
+    else:
+        wl = sg.get(args.workload)
+        res = run_prefill(args, m, sg, torch) if wl.is_prefill else run_decode(args, m, sg, torch)
     print(json.dumps(res), flush=True)
 
 

@@ -22,7 +22,8 @@ FORMATS = {"nvfp4": MOE_FMT_NVFP4, "mxfp4": MOE_FMT_MXFP4}
 
 # every symbol declared in include/moe_fp4.h
 EXPORTS = ("moe_block_bytes", "moe_block_layout", "moe_workspace_bytes", "moe_route", "moe_expert_decode",
-           "moe_layer_decode", "moe_expert_prefill", "moe_dequant_block", "moe_status_string", "moe_last_error")
+           "moe_layer_decode", "moe_expert_prefill", "moe_dequant_block", "moe_act_quant_fp8", "moe_gemv_fp8",
+           "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -67,6 +68,8 @@ def _load():
     L.moe_expert_prefill.restype = C.c_int
     L.moe_expert_prefill.argtypes = [D, P, I32, P, P, P, P, I32, P, SZ, C.POINTER(moe_prefill_debug), P]
     L.moe_dequant_block.restype = C.c_int; L.moe_dequant_block.argtypes = [D, P, P, P, P, P]
+    L.moe_act_quant_fp8.restype = C.c_int; L.moe_act_quant_fp8.argtypes = [P, I32, I32, I32, I32, P, P, P]
+    L.moe_gemv_fp8.restype = C.c_int; L.moe_gemv_fp8.argtypes = [P, P, P, I32, I32, P, P]
     L.moe_status_string.restype = C.c_char_p; L.moe_status_string.argtypes = [C.c_int]
     L.moe_last_error.restype = C.c_char_p; L.moe_last_error.argtypes = []
     return L
@@ -177,3 +180,14 @@ def expert_ptr_table(blocks, block_bytes: int | None = None):
         ptrs = [base + e * bb for e in range(blocks.shape[0])]
         dev = blocks.device
     return torch.tensor(ptrs, dtype=torch.int64, device=dev)
+
+
+MOE_SCALE_FLOOR, MOE_SCALE_CEIL = 0, 1
+
+
+def moe_act_quant_fp8(x, rows, cols, block, rule, codes, scales, stream=None):
+    _check(lib.moe_act_quant_fp8(_ptr(x), rows, cols, block, rule, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_gemv_fp8(W, row_scale, x, rows, cols, y, stream=None):
+    _check(lib.moe_gemv_fp8(_ptr(W), _ptr(row_scale), _ptr(x), rows, cols, _ptr(y), _stream(stream)))

@@ -223,6 +223,36 @@ const char* moe_status_string(int status) {
     }
 }
 
+int moe_act_quant_fp8(const float* x, int32_t rows, int32_t cols, int32_t block, int32_t rule, uint8_t* codes,
+                      uint8_t* scales, void* stream) {
+    if (rows < 0) return fail(MOE_ERR_ARG, "rows=%d is negative", rows);
+    if (block != 32 && block != 128) return fail(MOE_ERR_ARG, "block=%d (32 or 128)", block);
+    if (cols <= 0 || cols % block) return fail(MOE_ERR_ARG, "cols=%d must be a positive multiple of block=%d", cols, block);
+    if (rule != MOE_SCALE_FLOOR && rule != MOE_SCALE_CEIL) return fail(MOE_ERR_ARG, "unknown scale rule %d", rule);
+    if ((size_t)rows * cols > ((size_t)1 << 34)) return fail(MOE_ERR_ARG, "rows*cols too large");
+    if (rows == 0) return ok();
+    int r;
+    if ((r = check_ptr(x, 16, "x")) || (r = check_ptr(codes, 4, "codes")) || (r = check_ptr(scales, 1, "scales")))
+        return r;
+    return hip_status(moe::launch_act_quant_fp8(x, rows, cols, block, rule, codes, scales, (hipStream_t)stream),
+                      "act_quant_fp8 launch");
+}
+
+int moe_gemv_fp8(const uint8_t* W, const float* row_scale, const float* x, int32_t rows, int32_t cols, float* y,
+                 void* stream) {
+    if (rows < 0) return fail(MOE_ERR_ARG, "rows=%d is negative", rows);
+    if (cols <= 0) return fail(MOE_ERR_ARG, "cols=%d must be positive", cols);
+    if (!moe::gemv_fp8_supported(cols))
+        return fail(MOE_ERR_UNSUPPORTED, "cols=%d: no kernel (512*d, d in 1..8, 10, 12, 16)", cols);
+    if ((size_t)rows * cols >= ((size_t)1 << 31)) return fail(MOE_ERR_UNSUPPORTED, "rows*cols too large");
+    if (rows == 0) return ok();
+    int r;
+    if ((r = check_ptr(W, 16, "W")) || (r = check_ptr(row_scale, 4, "row_scale")) || (r = check_ptr(x, 16, "x")) ||
+        (r = check_ptr(y, 4, "y")))
+        return r;
+    return hip_status(moe::launch_gemv_fp8(W, row_scale, x, y, rows, cols, (hipStream_t)stream), "gemv_fp8 launch");
+}
+
 const char* moe_last_error(void) { return g_err; }
 
 }  // extern "C"

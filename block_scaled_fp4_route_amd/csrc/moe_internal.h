@@ -68,4 +68,13 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
                           const void* const* expert_ptrs, const int32_t* idx, const float* w, void* out,
                           int out_bf16, void* ws, const PrefillDebug* dbg, hipStream_t s);
 
+// ---- FP8 activation quantiser and row-scaled GEMV ----
+constexpr int kScaleFloor = 0;  // OCP MX shared exponent floor(log2 amax) - 8
+constexpr int kScaleCeil = 1;   // smallest exponent with amax <= 448 * 2^X
+hipError_t launch_act_quant_fp8(const float* x, int rows, int cols, int block, int rule, uint8_t* codes,
+                                uint8_t* scales, hipStream_t s);
+bool gemv_fp8_supported(int cols);
+hipError_t launch_gemv_fp8(const uint8_t* W, const float* rs, const float* x, float* y, int rows, int cols,
+                           hipStream_t s);
+
 }  // namespace moe

@@ -194,6 +194,41 @@ int moe_expert_prefill(const moe_desc *d, const float *x, int32_t T, const void 
                        size_t ws_bytes, const moe_prefill_debug *dbg, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* FP8 beside the MoE path                                                 */
+/* ---------------------------------------------------------------------- */
+
+#define MOE_SCALE_FLOOR 0 /* OCP MX: X = floor(log2 amax) - 8; quotients above 448 saturate */
+#define MOE_SCALE_CEIL 1  /* smallest X with amax <= 448 * 2^X; never saturates */
+
+/* Activation quantiser: FP8 E4M3 codes with one UE8M0 (power-of-two) scale
+ * per block of `block` consecutive values of a row ([D] "Three bugs", item
+ * 2: DeepSeek's activation quantiser, ue8m0 scales, FP8 out, checked
+ * bit-exact at 1, 17, 300 and 1024 rows; OCP MX: MXFP8 uses blocks of 32).
+ *   x       fp32 [rows][cols], 16-byte aligned
+ *   block   32 or 128; cols a positive multiple of block
+ *   rule    MOE_SCALE_FLOOR or MOE_SCALE_CEIL (shared exponent X of a block
+ *           from its largest magnitude amax, clamped to [-127, 127])
+ *   codes   out: uint8 [rows][cols], 4-byte aligned: E4M3 (OCP E4M3FN) of
+ *           v / 2^X rounded to nearest even, magnitudes clamped to 448;
+ *           negative values that round to zero give 0x80
+ *   scales  out: uint8 [rows][cols/block]: X + 127 (0 for an all-zero block)
+ * rows == 0 enqueues nothing and returns MOE_OK. No workspace. Inputs must be
+ * finite. Errors: MOE_ERR_ARG (pointers, sizes, block, rule). */
+int moe_act_quant_fp8(const float *x, int32_t rows, int32_t cols, int32_t block, int32_t rule, uint8_t *codes,
+                      uint8_t *scales, void *stream);
+
+/* Row-scaled FP8 matrix-vector product ([Q] "The engine", item 4: the FP8
+ * row-scaled matrix-vector kernel; [Q] "Why this model, of all models": the
+ * large dense matrices stored in FP8 with one scale per row):  y[r] = row_scale[r] * sum_c e4m3(W[r][c]) * x[c],
+ * accumulated in fp32.
+ *   W          uint8 E4M3 codes [rows][cols], row-major, 16-byte aligned
+ *   row_scale  fp32 [rows];  x  fp32 [cols], 16-byte aligned;  y  fp32 [rows]
+ * cols must be 512 * d with d in 1..8, 10, 12 or 16 (MOE_ERR_UNSUPPORTED
+ * otherwise); rows >= 0 (0 enqueues nothing). No workspace. */
+int moe_gemv_fp8(const uint8_t *W, const float *row_scale, const float *x, int32_t rows, int32_t cols, float *y,
+                 void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Test support and errors                                                 */
 /* ---------------------------------------------------------------------- */
 

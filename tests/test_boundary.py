@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_symbols():
     src = open(os.path.join(ROOT, "include", "moe_fp4.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -106,6 +106,26 @@ def test_layer_decode_argument_errors():
     assert call(a0=m.desc(2560, 640, 2048, 10, "nvfp4"), a9=1 << 24) == m.MOE_ERR_UNSUPPORTED  # E > 1024
     assert call(a0=m.desc(2560 + 256, 640, 512, 10, "nvfp4"), a9=1 << 24) == m.MOE_ERR_UNSUPPORTED  # H % 512
     assert call(a0=m.desc(2560, 640, 512, 0, "nvfp4")) == m.MOE_ERR_ARG
+
+
+def test_fp8_argument_errors():
+    q = m.moe_act_quant_fp8
+    q(FAKE, 0, 4096, 32, 0, FAKE, FAKE, 0)  # empty: nothing enqueued, MOE_OK
+    assert _err(q, FAKE, -1, 4096, 32, 0, FAKE, FAKE, 0) == m.MOE_ERR_ARG
+    assert _err(q, FAKE, 4, 4096, 64, 0, FAKE, FAKE, 0) == m.MOE_ERR_ARG       # block
+    assert _err(q, FAKE, 4, 4000, 128, 0, FAKE, FAKE, 0) == m.MOE_ERR_ARG      # cols % block
+    assert _err(q, FAKE, 4, 4096, 32, 2, FAKE, FAKE, 0) == m.MOE_ERR_ARG       # rule
+    assert _err(q, None, 4, 4096, 32, 0, FAKE, FAKE, 0) == m.MOE_ERR_ARG
+    assert _err(q, ODD, 4, 4096, 32, 0, FAKE, FAKE, 0) == m.MOE_ERR_ARG
+    assert _err(q, FAKE, 4, 4096, 32, 0, FAKE + 2, FAKE, 0) == m.MOE_ERR_ARG   # codes alignment
+    g = m.moe_gemv_fp8
+    g(FAKE, FAKE, FAKE, 0, 2560, FAKE, 0)
+    assert _err(g, FAKE, FAKE, FAKE, 8, 2560 + 64, FAKE, 0) == m.MOE_ERR_UNSUPPORTED
+    assert _err(g, FAKE, FAKE, FAKE, 8, 9 * 512, FAKE, 0) == m.MOE_ERR_UNSUPPORTED
+    assert _err(g, FAKE, FAKE, FAKE, 8, 20 * 512, FAKE, 0) == m.MOE_ERR_UNSUPPORTED
+    assert _err(g, FAKE, FAKE, FAKE, -1, 2560, FAKE, 0) == m.MOE_ERR_ARG
+    assert _err(g, FAKE + 8, FAKE, FAKE, 8, 2560, FAKE, 0) == m.MOE_ERR_ARG   # W alignment
+    assert _err(g, FAKE, FAKE, None, 8, 2560, FAKE, 0) == m.MOE_ERR_ARG
 
 
 def test_status_strings():
