@@ -22,10 +22,12 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // 1. activation quantiser
 //
-// Lane i converts the four values x[4i .. 4i+3]; the LPB = block/4 lanes of
-// a block are consecutive and aligned, so the block maximum is a butterfly
-// over LPB lanes. Shared exponent X from the exponent field of the block
-// maximum a = m * 2^(e - 127) (m in [1, 2), e = biased exponent):
+// Workgroup b covers 256 * kQuantPer float4 pieces; thread t takes
+// pieces 256 kQuantPer b + t + 256 j (j < kQuantPer), so for every j
+// the LPB = block/4 lanes of a block are consecutive and aligned and the
+// block maximum is a butterfly over LPB lanes. Shared exponent X from the
+// exponent field of the block maximum a = m * 2^(e - 127) (m in [1, 2),
+// e = biased exponent):
 //   floor rule (OCP MX):  X = floor(log2 a) - 8 = e - 135 (8 = largest
 //                         exponent of E4M3; quotients up to 511 saturate);
 //   ceil rule:            the smallest X with a <= 448 * 2^X: e - 135, plus
@@ -34,12 +36,11 @@ namespace moe {
 // and stored as the byte X + 127 (0 for an all-zero block). The quotients
 // v * 2^-X are exact (2^-X is a normal fp32 power of two), clamped to +-448
 // and rounded to nearest even by v_cvt_pk_fp8_f32 (OCP E4M3FN on gfx950).
+constexpr int kQuantPer = 1;  // float4 pieces per thread (more measured slower)
+
 template <int LPB>
-__global__ __launch_bounds__(256) void k_act_quant_fp8(const float4* __restrict__ x, size_t n4, int rule,
-                                                       uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n4) return;  // n4 is a multiple of LPB: whole blocks leave together
-    const float4 v = x[i];
+__device__ __forceinline__ void quant_piece(const float4 v, size_t i, int rule, uint32_t* __restrict__ codes,
+                                            uint8_t* __restrict__ scales) {
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
     for (int o = 1; o < LPB; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
@@ -55,10 +56,24 @@ __global__ __launch_bounds__(256) void k_act_quant_fp8(const float4* __restrict_
     if ((threadIdx.x & (LPB - 1)) == 0) scales[i / LPB] = a == 0.0f ? 0 : (uint8_t)(X + 127);
 }
 
+template <int LPB>
+__global__ __launch_bounds__(256) void k_act_quant_fp8(const float4* __restrict__ x, size_t n4, int rule,
+                                                       uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const size_t base = (size_t)blockIdx.x * 256 * kQuantPer + threadIdx.x;
+    float4 v[kQuantPer];
+#pragma unroll
+    for (int j = 0; j < kQuantPer; j++)
+        if (base + 256 * j < n4) v[j] = x[base + 256 * j];
+#pragma unroll
+    for (int j = 0; j < kQuantPer; j++)
+        // n4 is a multiple of LPB and 256 of LPB: whole blocks are in or out
+        if (base + 256 * j < n4) quant_piece<LPB>(v[j], base + 256 * j, rule, codes, scales);
+}
+
 hipError_t launch_act_quant_fp8(const float* x, int rows, int cols, int block, int rule, uint8_t* codes,
                                 uint8_t* scales, hipStream_t s) {
     const size_t n4 = (size_t)rows * cols / 4;
-    const dim3 grid((unsigned)((n4 + 255) / 256));
+    const dim3 grid((unsigned)((n4 + 256 * kQuantPer - 1) / (256 * kQuantPer)));
     const float4* x4 = reinterpret_cast<const float4*>(x);
     uint32_t* c4 = reinterpret_cast<uint32_t*>(codes);
     if (block == 32)
@@ -131,7 +146,7 @@ bool gemv_fp8_supported(int cols) {
 
 template <int D>
 static hipError_t launch_gemv_d(const uint8_t* W, const float* rs, const float* x, float* y, int rows, hipStream_t s) {
-    constexpr int R = D <= 4 ? 4 : (D <= 8 ? 2 : 1);
+    constexpr int R = D <= 8 ? 4 : 2;
     const unsigned waves = (unsigned)((rows + R - 1) / R);
     hipLaunchKernelGGL((k_gemv_fp8<D, R>), dim3((waves + 3) / 4), dim3(256), 0, s, W, rs, x, y, rows);
     return hipGetLastError();

@@ -1,0 +1,122 @@
+"""The launch configuration bench.py times: calls captured in a HIP graph.
+
+Each graph is replayed several times with the program's own eager work and
+synchronisations between the replays, and every replay must equal the eager
+result bit for bit (the kernels have no float atomics, and the library
+records no memset into a graph). One decode layer of the captured graph is
+also checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthgen as sg
+from gpu_helpers import NTHREADS, bf16_bits, host_blocks, layer_blocks, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_scaled_fp4_route_amd as m
+    return m
+
+
+def capture(fn):
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            fn()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    return g
+
+
+def eager_noise():
+    """Unrelated eager work between replays (allocations, kernels, a sync)."""
+    a = torch.randn(1 << 20, device="cuda")
+    (a * 2.0 + 1.0).sum().item()
+
+
+def test_decode_layers_in_a_graph(m, orc):
+    """Three full Qwen-shaped layers (512 NVFP4 experts + bf16 shared expert
+    each) through moe_layer_decode, one workspace, as the bench's graph."""
+    wl = sg.get("qwen_decode")
+    L = 3
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    blocks = [layer_blocks(wl, l) for l in range(L)]
+    ptrs = [m.expert_ptr_table(b) for b in blocks]
+    Wr = [sg.router_weights(wl, l, device="cuda") for l in range(L)]
+    shared = [[t.contiguous() for t in sg.shared_expert(wl, l, device="cuda")] for l in range(L)]
+    xs = [sg.activations(wl, 9, l, T=1, device="cuda").view(-1) for l in range(L)]
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    ys = [torch.empty(wl.H, device="cuda") for _ in range(L)]
+    idx = [torch.empty(wl.k, dtype=torch.int32, device="cuda") for _ in range(L)]
+    w = [torch.empty(wl.k, device="cuda") for _ in range(L)]
+
+    def run():
+        for l in range(L):
+            m.moe_layer_decode(d, xs[l], Wr[l], ptrs[l], shared[l], ys[l], idx[l], w[l], ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref_y = [y.clone() for y in ys]
+    ref_i = [i.clone() for i in idx]
+    ref_w = [v.clone() for v in w]
+    g = capture(run)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        for i in idx:
+            i.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(ys[l].view(torch.int32), ref_y[l].view(torch.int32)), (rep, l)
+            assert torch.equal(idx[l], ref_i[l]) and torch.equal(w[l].view(torch.int32), ref_w[l].view(torch.int32))
+        eager_noise()
+    # the last layer of the replayed graph against the oracle
+    l = L - 1
+    _, oi, ow = orc.route(xs[l].cpu().numpy(), Wr[l].cpu().numpy(), wl.k)
+    gi = idx[l].cpu().numpy()
+    assert (gi == oi[0]).all()
+    hb = host_blocks(blocks[l], gi)
+    ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, xs[l].cpu().numpy(), [hb[int(e)] for e in gi], ow[0],
+                            shared=[bf16_bits(s) for s in shared[l]], nthreads=NTHREADS)
+    assert rel_err(ys[l].cpu().numpy(), ref) <= 1e-4
+
+
+def test_fp8_kernels_in_a_graph(m, orc):
+    rows, cols = 300, 4096
+    x = sg.fp8_activations(rows, cols, 11, device="cuda")
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    W = sg.fp8_matrix(2560, 8192, 2, device="cuda")
+    s = sg.fp8_row_scales(2560, 2, device="cuda")
+    v = sg.fp8_vector(8192, 2, device="cuda")
+    y = torch.empty(2560, device="cuda")
+
+    def run():
+        m.moe_act_quant_fp8(x, rows, cols, 32, m.MOE_SCALE_FLOOR, codes, scales)
+        m.moe_gemv_fp8(W, s, v, 2560, 8192, y)
+
+    run()
+    torch.cuda.synchronize()
+    rc, rs, ry = codes.clone(), scales.clone(), y.clone()
+    g = capture(run)
+    for rep in range(3):
+        codes.fill_(0x7F)
+        scales.fill_(0xFF)
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(codes, rc) and torch.equal(scales, rs), rep
+        assert torch.equal(y.view(torch.int32), ry.view(torch.int32)), rep
+        eager_noise()
+    oc, osc = orc.quant_fp8_rows(x.cpu().numpy(), block=32, rule=0)
+    assert (codes.cpu().numpy() == oc).all() and (scales.cpu().numpy() == osc).all()
+    assert rel_err(y.cpu().numpy(), orc.gemv_fp8(W.cpu().numpy(), s.cpu().numpy(), v.cpu().numpy())) <= 1e-4
