@@ -23,6 +23,7 @@ FORMATS = {"nvfp4": MOE_FMT_NVFP4, "mxfp4": MOE_FMT_MXFP4}
 # every symbol declared in include/moe_fp4.h
 EXPORTS = ("moe_block_bytes", "moe_block_layout", "moe_workspace_bytes", "moe_route", "moe_expert_decode",
            "moe_layer_decode", "moe_expert_prefill", "moe_dequant_block", "moe_act_quant_fp8", "moe_gemv_fp8",
+           "moe_tier_create", "moe_tier_destroy", "moe_tier_update", "moe_tier_get_stats", "moe_tier_slot_of",
            "moe_status_string", "moe_last_error")
 
 
@@ -43,6 +44,11 @@ class moe_shared(C.Structure):
 class moe_prefill_debug(C.Structure):
     _fields_ = [("x_bf16", C.c_void_p), ("x_codes", C.c_void_p), ("x_scales", C.c_void_p), ("h_pre", C.c_void_p),
                 ("h_q", C.c_void_p), ("perm", C.c_void_p), ("off", C.c_void_p)]
+
+
+class moe_tier_stats(C.Structure):
+    _fields_ = [("resident", C.c_int64), ("pending", C.c_int64), ("hits", C.c_int64), ("misses", C.c_int64),
+                ("promotions", C.c_int64), ("evictions", C.c_int64)]
 
 
 def _load():
@@ -70,6 +76,12 @@ def _load():
     L.moe_dequant_block.restype = C.c_int; L.moe_dequant_block.argtypes = [D, P, P, P, P, P]
     L.moe_act_quant_fp8.restype = C.c_int; L.moe_act_quant_fp8.argtypes = [P, I32, I32, I32, I32, P, P, P]
     L.moe_gemv_fp8.restype = C.c_int; L.moe_gemv_fp8.argtypes = [P, P, P, I32, I32, P, P]
+    L.moe_tier_create.restype = C.c_int
+    L.moe_tier_create.argtypes = [D, I32, P, P, I32, P, C.POINTER(P)]
+    L.moe_tier_destroy.restype = C.c_int; L.moe_tier_destroy.argtypes = [P]
+    L.moe_tier_update.restype = C.c_int; L.moe_tier_update.argtypes = [P, P, I32, P]
+    L.moe_tier_get_stats.restype = C.c_int; L.moe_tier_get_stats.argtypes = [P, C.POINTER(moe_tier_stats)]
+    L.moe_tier_slot_of.restype = I32; L.moe_tier_slot_of.argtypes = [P, I32, I32]
     L.moe_status_string.restype = C.c_char_p; L.moe_status_string.argtypes = [C.c_int]
     L.moe_last_error.restype = C.c_char_p; L.moe_last_error.argtypes = []
     return L
@@ -191,3 +203,39 @@ def moe_act_quant_fp8(x, rows, cols, block, rule, codes, scales, stream=None):
 
 def moe_gemv_fp8(W, row_scale, x, rows, cols, y, stream=None):
     _check(lib.moe_gemv_fp8(_ptr(W), _ptr(row_scale), _ptr(x), rows, cols, _ptr(y), _stream(stream)))
+
+
+class ExpertTier:
+    """Owner of a moe_tier (pinned host blocks + HBM slots + the per-layer
+    pointer tables); table(layer) is the expert_ptrs argument of the decode
+    entry points."""
+
+    def __init__(self, d, layers, host_blocks, slots, n_slots, table):
+        self.d, self.E = d, d.E
+        self._keep = (host_blocks, slots, table)
+        h = C.c_void_p()
+        _check(lib.moe_tier_create(C.byref(d), layers, _ptr(host_blocks), _ptr(slots), n_slots, _ptr(table),
+                                   C.byref(h)))
+        self.h = h
+        self.table_tensor = table
+
+    def table(self, layer):
+        return self.table_tensor[layer * self.E:(layer + 1) * self.E]
+
+    def update(self, idx_host, max_promote, stream=None):
+        import numpy as np
+        a = np.ascontiguousarray(idx_host, dtype=np.int32)
+        _check(lib.moe_tier_update(self.h, a.ctypes.data_as(C.c_void_p), max_promote, _stream(stream)))
+
+    def stats(self) -> dict:
+        st = moe_tier_stats()
+        _check(lib.moe_tier_get_stats(self.h, C.byref(st)))
+        return {f: getattr(st, f) for f, _ in moe_tier_stats._fields_}
+
+    def slot_of(self, layer, expert) -> int:
+        return int(lib.moe_tier_slot_of(self.h, layer, expert))
+
+    def close(self):
+        if self.h:
+            lib.moe_tier_destroy(self.h)
+            self.h = None

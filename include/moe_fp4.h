@@ -229,6 +229,70 @@ int moe_gemv_fp8(const uint8_t *W, const float *row_scale, const float *x, int32
                  void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Expert tier: pinned host blocks with an HBM slot cache                  */
+/* ---------------------------------------------------------------------- */
+
+/* ([Q] "The engine", items 2-3: an LRU cache of experts in front of the slow
+ * tier, GPU slots, and copies into them overlapped with compute; [D] "Making
+ * it faster".) Every expert block of `layers` layers lives in pinned host
+ * memory; n_slots HBM slots hold the most recently routed ones. The tier owns
+ * the per-layer pointer tables the decode entry points take
+ * (expert_ptrs = table + layer * E): each entry points at the expert's HBM
+ * slot or, for experts not in HBM, at its pinned host block, which the
+ * kernels then read in place over PCIe (no copy, no host synchronisation).
+ *
+ * Unlike the compute entry points, the tier is a resource-owning object: it
+ * creates one copy stream and a few events, allocates a small pinned staging
+ * array and host-side state, and moe_tier_create synchronises once (initial
+ * table). Every decode launch that reads the table must be on the
+ * compute_stream given to moe_tier_update (the tier orders its table writes
+ * with those launches); not for use under graph capture. */
+typedef struct moe_tier moe_tier;
+typedef struct {
+    int64_t resident;   /* experts whose table entry points at their HBM slot */
+    int64_t pending;    /* experts being copied (entry switches at the next update) */
+    int64_t hits;       /* routed (layer, slot) uses found resident, over all updates */
+    int64_t misses;     /* routed uses read from host memory */
+    int64_t promotions; /* blocks copied into slots */
+    int64_t evictions;  /* experts moved back to their host blocks */
+} moe_tier_stats;
+
+/*   host_blocks  pinned host memory (hipHostMalloc or equivalent, mapped at the
+ *                same address on the device): layers * E blocks of
+ *                moe_block_bytes(d), layer-major, 256-byte aligned
+ *   slots        device memory for n_slots blocks (NULL if n_slots == 0)
+ *   table        device memory for layers * E pointers, 8-byte aligned;
+ *                filled by the tier (all entries start at the host blocks)
+ * Errors: MOE_ERR_ARG (sizes, alignment, memory not pinned / not on the
+ * device), MOE_ERR_HIP. */
+int moe_tier_create(const moe_desc *d, int32_t layers, void *host_blocks, void *slots, int32_t n_slots, void **table,
+                    moe_tier **out);
+
+/* Waits for the tier's own copies, then frees its streams, events and state
+ * (not the caller's buffers). Work the caller enqueued that reads the table
+ * must be finished first. */
+int moe_tier_destroy(moe_tier *t);
+
+/* After a decode step: idx_host [layers][k] is that step's routing (host
+ * memory, e.g. read back asynchronously by the caller; indices outside
+ * [0, E) are ignored). Enqueued on compute_stream, in this order: the table
+ * entries of the previous update's newcomers switch to their slots (after
+ * their copies, by event); up to max_promote experts of this step that are
+ * not in HBM take a free slot or the slot of the least recently used expert
+ * that this step did not use, whose entry first returns to its host block;
+ * then, on the tier's copy stream, once the compute stream has passed those
+ * entries, the newcomers' blocks are copied into their slots (overlapping the
+ * compute stream). Nothing here waits on the host except for a staging
+ * buffer four updates old. */
+int moe_tier_update(moe_tier *t, const int32_t *idx_host, int32_t max_promote, void *compute_stream);
+
+/* Counters and residency (host state, no device access). */
+int moe_tier_get_stats(const moe_tier *t, moe_tier_stats *out);
+
+/* Slot of (layer, expert) if its table entry points at HBM, else -1. */
+int32_t moe_tier_slot_of(const moe_tier *t, int32_t layer, int32_t expert);
+
+/* ---------------------------------------------------------------------- */
 /* Test support and errors                                                 */
 /* ---------------------------------------------------------------------- */
 

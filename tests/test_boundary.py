@@ -128,6 +128,25 @@ def test_fp8_argument_errors():
     assert _err(g, FAKE, FAKE, None, 8, 2560, FAKE, 0) == m.MOE_ERR_ARG
 
 
+def test_tier_argument_errors():
+    import ctypes
+    d = m.desc(2560, 640, 64, 10, "nvfp4")
+    out = ctypes.c_void_p()
+    L = m.lib
+    assert L.moe_tier_create(ctypes.byref(d), 2, FAKE, FAKE, 4, FAKE, None) == m.MOE_ERR_ARG       # out NULL
+    assert L.moe_tier_create(ctypes.byref(d), 0, FAKE, FAKE, 4, FAKE, ctypes.byref(out)) == m.MOE_ERR_ARG
+    assert L.moe_tier_create(ctypes.byref(d), 2, FAKE, FAKE, -1, FAKE, ctypes.byref(out)) == m.MOE_ERR_ARG
+    assert L.moe_tier_create(ctypes.byref(d), 2, None, FAKE, 4, FAKE, ctypes.byref(out)) == m.MOE_ERR_ARG
+    assert L.moe_tier_create(ctypes.byref(d), 2, FAKE, None, 4, FAKE, ctypes.byref(out)) == m.MOE_ERR_ARG
+    assert L.moe_tier_create(ctypes.byref(d), 2, FAKE + 16, FAKE, 4, FAKE, ctypes.byref(out)) == m.MOE_ERR_ARG
+    bad = m.desc(2560, 640, 64, 11, 7)
+    assert L.moe_tier_create(ctypes.byref(bad), 2, FAKE, FAKE, 4, FAKE, ctypes.byref(out)) == m.MOE_ERR_ARG
+    assert out.value is None
+    assert L.moe_tier_update(None, FAKE, 1, None) == m.MOE_ERR_ARG
+    assert L.moe_tier_destroy(None) == m.MOE_OK
+    assert L.moe_tier_slot_of(None, 0, 0) == -1
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert m.lib.moe_status_string(s)
