@@ -422,6 +422,113 @@ def run_fp8(args, m, sg, torch):
     return res
 
 
+def run_tier(args, m, sg, torch):
+    """Qwen-shaped decode with every expert in pinned host memory behind an
+    HBM slot cache (moe_tier): per token, the layers read through the tier's
+    tables (misses over PCIe, in place), the routing is read back, and the
+    tier promotes the step's misses. Reported for a slot pool of
+    --tier-slots experts (default a quarter of all) and with no slots (every
+    expert read from host memory)."""
+    import numpy as np
+    wl = sg.get("qwen_decode")
+    L = args.tier_layers
+    E, k, bb = wl.E, wl.k, wl.block_bytes
+    d = m.desc(wl.H, wl.I, E, k, wl.fmt)
+    t0 = time.time()
+    host = torch.empty((L * E, bb), dtype=torch.uint8, pin_memory=True)
+    buf = torch.empty((E, bb), dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        sg.fill_layer_blocks(wl, l, buf)
+        host[l * E:(l + 1) * E].copy_(buf)
+    del buf
+    Wr = [sg.router_weights(wl, l, device="cuda") for l in range(L)]
+    # skewed routing: the router rows of a seeded set of hot experts per layer
+    # scaled by tier_hot_scale, so those experts win the top-k more often
+    # (the synthetic router alone routes almost uniformly)
+    hot = max(0, args.tier_hot)
+    Wr_hot = []
+    for l in range(L):
+        perm = torch.argsort(sg.words(sg.stream_key(77, l), E, device="cuda"))
+        sc = torch.ones(E, device="cuda")
+        sc[perm[:hot]] = args.tier_hot_scale
+        Wr_hot.append((Wr[l] * sc[:, None]).contiguous())
+    shared = [[t.contiguous() for t in sg.shared_expert(wl, l, device="cuda")] for l in range(L)]
+    K, W = args.steps, args.warmup
+    xs = [[sg.activations(wl, s, l, T=1, device="cuda").view(-1) for l in range(L)] for s in range(W + K)]
+    log(f"[bench] tier: {L} layers x {E} experts in pinned host memory ({host.numel() / 2**30:.1f} GiB), "
+        f"set up in {time.time() - t0:.1f} s")
+    # host -> device copy rate of pinned memory (1 GiB)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src = host.view(-1)[:1 << 30]
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d = 3 * (1 << 30) / (time.perf_counter() - c0) / 1e9
+    del dst
+
+    def run(n_slots, Wr):
+        slots = torch.empty((n_slots, bb), dtype=torch.uint8, device="cuda") if n_slots else None
+        table = torch.empty(L * E, dtype=torch.int64, device="cuda")
+        tier = m.ExpertTier(d, L, host, slots, n_slots, table)
+        ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+        y = torch.empty(wl.H, device="cuda")
+        idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((L, k), device="cuda")
+        idx_h = torch.empty((L, k), dtype=torch.int32, pin_memory=True)
+        try:
+            def step(s):
+                for l in range(L):
+                    m.moe_layer_decode(d, xs[s][l], Wr[l], tier.table(l), shared[l], y, idx[l], w[l], ws)
+                idx_h.copy_(idx, non_blocking=True)
+                torch.cuda.current_stream().synchronize()  # the routing reaches the host
+                tier.update(idx_h.numpy(), args.tier_promote)
+            for s in range(W):
+                step(s)
+            torch.cuda.synchronize()
+            st0 = tier.stats()
+            c0 = time.perf_counter()
+            for s in range(W, W + K):
+                step(s)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - c0
+            st = tier.stats()
+        finally:
+            tier.close()
+        hits, misses = st["hits"] - st0["hits"], st["misses"] - st0["misses"]
+        return {"tokens_per_s": round(K / el, 2), "ms_per_token": round(el / K * 1e3, 3),
+                "hit_rate": round(hits / max(1, hits + misses), 4),
+                "host_read_GBps": round(misses * bb / el / 1e9, 2),
+                "promoted_GBps": round((st["promotions"] - st0["promotions"]) * bb / el / 1e9, 2),
+                "slots": n_slots}
+    n_slots = args.tier_slots if args.tier_slots >= 0 else (L * E) // 4
+    tiered = run(n_slots, Wr)
+    host_only = run(0, Wr)
+    skewed = {"hot_experts_per_layer": hot, "hot_router_scale": args.tier_hot_scale,
+              "tiered": run(n_slots, Wr_hot), "host_only": run(0, Wr_hot)}
+    pcie_peak = 64.0  # PCIe 5.0 x16, one direction
+    res = {
+        "metric": METRIC, "value": tiered["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": tiered["ms_per_token"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded SplitMix64; random-code FP4 experts, no trained weights)",
+        "config": {"workload": "qwen_tier", "layers": L, "experts": E, "top_k": k, "hidden": wl.H,
+                   "intermediate": wl.I, "weights": "nvfp4", "shared_expert": "bf16 (HBM)",
+                   "expert_store": "pinned host memory + HBM slot cache", "slots": n_slots,
+                   "max_promote_per_token": args.tier_promote, "routing_readback": "per token",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "decode layers reading missed experts from pinned host memory", "bound": "pcie",
+                     "achieved": host_only["host_read_GBps"], "peak": pcie_peak, "unit": "GB/s",
+                     "frac": round(host_only["host_read_GBps"] / pcie_peak, 4), "traffic": None,
+                     "bytes_per_launch": k * bb, "note": "achieved = expert bytes read over the host link per second "
+                     "with no slots (every routed expert a miss)"},
+        "tiered": tiered, "host_only": host_only, "skewed_routing": skewed,
+        "h2d_copy_GBps_measured": round(h2d, 2),
+    }
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +538,11 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="layer replicas to rotate through (cold timing)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tier-layers", type=int, default=8, help="qwen_tier: layers in pinned host memory")
+    ap.add_argument("--tier-slots", type=int, default=-1, help="qwen_tier: HBM slots (default: a quarter)")
+    ap.add_argument("--tier-promote", type=int, default=16, help="qwen_tier: promotions per token at most")
+    ap.add_argument("--tier-hot", type=int, default=48, help="qwen_tier: hot experts per layer (skewed run)")
+    ap.add_argument("--tier-hot-scale", type=float, default=3.0, help="qwen_tier: router scale of hot experts")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 4 device copies of 1 GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -455,6 +567,8 @@ def main():
         return
     if args.workload in FP8_WORKLOADS:
         res = run_fp8(args, m, sg, torch)
+    elif args.workload == "qwen_tier":
+        res = run_tier(args, m, sg, torch)
     else:
         wl = sg.get(args.workload)
         res = run_prefill(args, m, sg, torch) if wl.is_prefill else run_decode(args, m, sg, torch)
