@@ -44,7 +44,7 @@ bool plan_decode(int fmt, int H, int I, DecodePlan* p) {
     if (H % 512 || H / 512 < 1 || H / 512 > 8) return false;
     if (I % G || I < 16 || I > kMaxI) return false;
     p->gate_D = H / 512;
-    p->gate_P = p->gate_D <= 5 ? 4 : 2;
+    p->gate_P = p->gate_D <= 4 ? 4 : 2;  // 2 pairs per wave at H = 2560: 1 and 4 measured slower
     p->gate_wg_per_slot = (I + 4 * p->gate_P - 1) / (4 * p->gate_P);
     const int KD = I / 8;
     if (KD <= 16 * 8) {
@@ -987,7 +987,7 @@ static hipError_t launch_expert(const DecodePlan& p, DecodeArgs& a, hipStream_t 
     const int n_gate = a.k * a.gt_r + (a.has_shared ? a.gt_s : 0);
 #define GU(GD, GP) case GD: hipLaunchKernelGGL((k_gateup<FMT, GD, GP>), dim3(n_gate), dim3(256), 0, s, a); break;
     switch (p.gate_D) {
-        GU(1, 4) GU(2, 4) GU(3, 4) GU(4, 4) GU(5, 4) GU(6, 2) GU(7, 2) GU(8, 2)
+        GU(1, 4) GU(2, 4) GU(3, 4) GU(4, 4) GU(5, 2) GU(6, 2) GU(7, 2) GU(8, 2)
         default: return hipErrorInvalidValue;
     }
 #undef GU
@@ -1032,7 +1032,7 @@ static hipError_t launch_layer(const DecodePlan& p, DecodeArgs& a, hipStream_t s
         case 2: e = launch_topk_gateup<FMT, 2, 4>(p, a, s); break;
         case 3: e = launch_topk_gateup<FMT, 3, 4>(p, a, s); break;
         case 4: e = launch_topk_gateup<FMT, 4, 4>(p, a, s); break;
-        case 5: e = launch_topk_gateup<FMT, 5, 4>(p, a, s); break;
+        case 5: e = launch_topk_gateup<FMT, 5, 2>(p, a, s); break;
         case 6: e = launch_topk_gateup<FMT, 6, 2>(p, a, s); break;
         case 7: e = launch_topk_gateup<FMT, 7, 2>(p, a, s); break;
         case 8: e = launch_topk_gateup<FMT, 8, 2>(p, a, s); break;
