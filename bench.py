@@ -529,6 +529,99 @@ def run_tier(args, m, sg, torch):
     return res
 
 
+def run_speculate(args, m, sg, torch):
+    """Speculative next-layer routing on the 48-layer Qwen-shaped decode: while
+    layer l runs, a second stream routes layer l+1's router on layer l's input
+    and reads the guessed experts' blocks (moe_expert_prefetch) so they sit in
+    the MALL when layer l+1 needs them. The layer inputs are a synthetic
+    residual stream, x_l = x_(l-1) + 0.5 e_l with fresh N(0, 1) draws e_l, so
+    that consecutive layers' inputs are correlated (with independent inputs
+    per layer any guess would hit by chance only). Both runs (with and without
+    speculation) are HIP graphs of the same K steps."""
+    import numpy as np
+    wl = sg.get("qwen_decode")
+    model = DecodeModel(m, sg, wl)
+    L, K, W = wl.layers, args.steps, args.warmup
+    d = model.d
+    xs = []
+    for s in range(W + K):
+        row, prev = [], None
+        for l in range(L):
+            e = sg.activations(wl, s, l, T=1, device="cuda").view(-1)
+            prev = e if prev is None else prev + 0.5 * e
+            row.append(prev.contiguous())
+        xs.append(row)
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    wsr = m.alloc_workspace(d, 1, m.MOE_MODE_ROUTE)
+    y = torch.empty(wl.H, device="cuda")
+    idx = torch.empty((W + K, L, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, wl.k), device="cuda")
+    guess = torch.full((W + K, L, wl.k), -1, dtype=torch.int32, device="cuda")
+    gw = torch.empty((L, wl.k), device="cuda")
+    sink = torch.empty(m.moe_prefetch_sink_bytes(d, wl.k) // 4 * L, dtype=torch.int32, device="cuda")
+    nsink = m.moe_prefetch_sink_bytes(d, wl.k) // 4
+    s2 = torch.cuda.Stream()
+
+    def step(s, spec):
+        cs = torch.cuda.current_stream()
+        for l in range(L):
+            if spec and l + 1 < L:
+                ev = torch.cuda.Event()
+                ev.record(cs)  # layer l's input exists from here on
+                s2.wait_event(ev)
+                m.moe_route(d, xs[s][l], 1, model.Wr[l + 1], guess[s, l + 1], gw[l + 1], None, wsr, stream=s2)
+                m.moe_expert_prefetch(d, model.ptrs[l + 1], guess[s, l + 1], wl.k, sink[l * nsink:(l + 1) * nsink],
+                                      stream=s2)
+            m.moe_layer_decode(d, xs[s][l], model.Wr[l], model.ptrs[l], model.shared[l], y, idx[s, l], w[l], ws)
+        if spec:
+            cs.wait_stream(s2)
+
+    def timed(spec):
+        for s in range(W):
+            step(s, spec)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for s in range(W, W + K):
+                    step(s, spec)
+        torch.cuda.current_stream().wait_stream(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    ms_plain = timed(False)
+    ms_spec = timed(True)
+    gi, ai = guess[W:, 1:].cpu().numpy(), idx[W:, 1:].cpu().numpy()
+    hit = np.mean([len(set(gi[s, l]) & set(ai[s, l])) / wl.k for s in range(K) for l in range(L - 1)])
+    experts, router, shared, act = bytes_per_layer(wl)
+    layer_bytes = experts + router + shared + act
+    res = {
+        "metric": METRIC, "value": round(1e3 / ms_spec, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_spec, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded SplitMix64; residual-stream inputs x_l = x_(l-1) + 0.5 e_l)",
+        "config": {"workload": "qwen_speculate", "layers": L, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
+                   "intermediate": wl.I, "weights": "nvfp4", "shared_expert": "bf16", "launch": "hip_graph",
+                   "speculation": "moe_route(x_l, Wr_(l+1)) + moe_expert_prefetch on a second stream",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "48 decode layers (moe_layer_decode) with speculative prefetch beside them",
+                     "bound": "hbm", "achieved": round(layer_bytes * L / (ms_spec * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(layer_bytes * L / (ms_spec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": layer_bytes * L},
+        "without_speculation": {"tokens_per_s": round(1e3 / ms_plain, 2), "ms_per_step": round(ms_plain, 4)},
+        "guess_hit_rate": round(float(hit), 4),
+    }
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -569,6 +662,8 @@ def main():
         res = run_fp8(args, m, sg, torch)
     elif args.workload == "qwen_tier":
         res = run_tier(args, m, sg, torch)
+    elif args.workload == "qwen_speculate":
+        res = run_speculate(args, m, sg, torch)
     else:
         wl = sg.get(args.workload)
         res = run_prefill(args, m, sg, torch) if wl.is_prefill else run_decode(args, m, sg, torch)

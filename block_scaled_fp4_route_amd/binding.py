@@ -23,7 +23,7 @@ FORMATS = {"nvfp4": MOE_FMT_NVFP4, "mxfp4": MOE_FMT_MXFP4}
 # every symbol declared in include/moe_fp4.h
 EXPORTS = ("moe_block_bytes", "moe_block_layout", "moe_workspace_bytes", "moe_route", "moe_expert_decode",
            "moe_layer_decode", "moe_expert_prefill", "moe_dequant_block", "moe_act_quant_fp8", "moe_gemv_fp8",
-           "moe_tier_create", "moe_tier_destroy", "moe_tier_update", "moe_tier_get_stats", "moe_tier_slot_of",
+           "moe_prefetch_sink_bytes", "moe_expert_prefetch", "moe_tier_create", "moe_tier_destroy", "moe_tier_update", "moe_tier_get_stats", "moe_tier_slot_of",
            "moe_status_string", "moe_last_error")
 
 
@@ -76,6 +76,8 @@ def _load():
     L.moe_dequant_block.restype = C.c_int; L.moe_dequant_block.argtypes = [D, P, P, P, P, P]
     L.moe_act_quant_fp8.restype = C.c_int; L.moe_act_quant_fp8.argtypes = [P, I32, I32, I32, I32, P, P, P]
     L.moe_gemv_fp8.restype = C.c_int; L.moe_gemv_fp8.argtypes = [P, P, P, I32, I32, P, P]
+    L.moe_prefetch_sink_bytes.restype = SZ; L.moe_prefetch_sink_bytes.argtypes = [D, I32]
+    L.moe_expert_prefetch.restype = C.c_int; L.moe_expert_prefetch.argtypes = [D, P, P, I32, P, SZ, P]
     L.moe_tier_create.restype = C.c_int
     L.moe_tier_create.argtypes = [D, I32, P, P, I32, P, C.POINTER(P)]
     L.moe_tier_destroy.restype = C.c_int; L.moe_tier_destroy.argtypes = [P]
@@ -239,3 +241,12 @@ class ExpertTier:
         if self.h:
             lib.moe_tier_destroy(self.h)
             self.h = None
+
+
+def moe_prefetch_sink_bytes(d: moe_desc, n: int) -> int:
+    return int(lib.moe_prefetch_sink_bytes(C.byref(d), n))
+
+
+def moe_expert_prefetch(d, expert_ptrs, idx, n, sink, stream=None):
+    _check(lib.moe_expert_prefetch(C.byref(d), _ptr(expert_ptrs), _ptr(idx), n, _ptr(sink),
+                                   sink.numel() * sink.element_size(), _stream(stream)))

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libmoe_fp4.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kernels_decode.hip", "kernels_route.hip", "kernels_prefill.hip", "kernels_fp8.hip", "moe_api.cpp", "moe_tier.cpp"]
+SOURCES = ["kernels_decode.hip", "kernels_route.hip", "kernels_prefill.hip", "kernels_fp8.hip", "kernels_prefetch.hip", "moe_api.cpp", "moe_tier.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed-FP32 VALU forms are kept out of all device code

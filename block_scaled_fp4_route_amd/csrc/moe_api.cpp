@@ -253,6 +253,27 @@ int moe_gemv_fp8(const uint8_t* W, const float* row_scale, const float* x, int32
     return hip_status(moe::launch_gemv_fp8(W, row_scale, x, y, rows, cols, (hipStream_t)stream), "gemv_fp8 launch");
 }
 
+size_t moe_prefetch_sink_bytes(const moe_desc* d, int32_t n) {
+    const size_t bb = moe_block_bytes(d);
+    if (!bb || n < 1 || n > 1024) return 0;
+    return (size_t)n * moe::prefetch_chunks(bb) * sizeof(uint32_t);
+}
+
+int moe_expert_prefetch(const moe_desc* d, const void* const* expert_ptrs, const int32_t* idx, int32_t n,
+                        uint32_t* sink, size_t sink_bytes, void* stream) {
+    int r;
+    if ((r = check_desc(d))) return r;
+    if (n < 1 || n > 1024) return fail(MOE_ERR_ARG, "n=%d (1..1024)", n);
+    if ((r = check_ptr(expert_ptrs, 8, "expert_ptrs")) || (r = check_ptr(idx, 4, "idx")) ||
+        (r = check_ptr(sink, 4, "sink")))
+        return r;
+    const size_t need = moe_prefetch_sink_bytes(d, n);
+    if (sink_bytes < need) return fail(MOE_ERR_ARG, "sink has %zu bytes, needs %zu", sink_bytes, need);
+    return hip_status(moe::launch_prefetch(expert_ptrs, idx, n, d->E, moe_block_bytes(d), sink,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                      "prefetch launch");
+}
+
 const char* moe_last_error(void) { return g_err; }
 
 }  // extern "C"

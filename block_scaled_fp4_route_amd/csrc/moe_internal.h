@@ -77,4 +77,9 @@ bool gemv_fp8_supported(int cols);
 hipError_t launch_gemv_fp8(const uint8_t* W, const float* rs, const float* x, float* y, int rows, int cols,
                            hipStream_t s);
 
+// ---- speculative expert prefetch ----
+int prefetch_chunks(size_t block_bytes);
+hipError_t launch_prefetch(const void* const* ptrs, const int32_t* idx, int n, int E, size_t block_bytes,
+                           uint32_t* sink, hipStream_t s);
+
 }  // namespace moe

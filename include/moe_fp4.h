@@ -229,6 +229,25 @@ int moe_gemv_fp8(const uint8_t *W, const float *row_scale, const float *x, int32
                  void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Speculative expert prefetch                                             */
+/* ---------------------------------------------------------------------- */
+
+/* ([Q] "The engine", item 3: guess the next layer's experts and read them
+ * while the GPU is busy; [D] "Making it faster": predicting the next layer's
+ * experts.) Reads the whole blocks of experts idx[0..n) (device int32; an
+ * index outside [0, E) is skipped) through expert_ptrs so that they sit in
+ * the GPU's last-level cache when a following launch needs them. The guess is
+ * the caller's: typically moe_route with the next layer's router on this
+ * layer's input, on a second stream. The read is made observable: sink
+ * (device, 4-byte aligned, at least moe_prefetch_sink_bytes(d, n) bytes)
+ * receives, for expert j and 64 KiB chunk c of its block, the XOR of the
+ * chunk's 32-bit words at sink[j * nchunks + c] (0 for a skipped index).
+ * n in 1..1024. Errors: MOE_ERR_ARG. */
+size_t moe_prefetch_sink_bytes(const moe_desc *d, int32_t n);
+int moe_expert_prefetch(const moe_desc *d, const void *const *expert_ptrs, const int32_t *idx, int32_t n,
+                        uint32_t *sink, size_t sink_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Expert tier: pinned host blocks with an HBM slot cache                  */
 /* ---------------------------------------------------------------------- */
 

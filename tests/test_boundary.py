@@ -147,6 +147,19 @@ def test_tier_argument_errors():
     assert L.moe_tier_slot_of(None, 0, 0) == -1
 
 
+def test_prefetch_argument_errors():
+    d = m.desc(2560, 640, 64, 10, "nvfp4")
+    nch = -(-m.moe_block_bytes(d) // 65536)
+    assert m.moe_prefetch_sink_bytes(d, 10) == 10 * nch * 4
+    assert m.moe_prefetch_sink_bytes(d, 0) == 0
+    L = m.lib
+    import ctypes
+    assert L.moe_expert_prefetch(ctypes.byref(d), FAKE, FAKE, 0, FAKE, 1 << 20, None) == m.MOE_ERR_ARG
+    assert L.moe_expert_prefetch(ctypes.byref(d), FAKE + 4, FAKE, 10, FAKE, 1 << 20, None) == m.MOE_ERR_ARG
+    assert L.moe_expert_prefetch(ctypes.byref(d), FAKE, FAKE, 10, FAKE, 16, None) == m.MOE_ERR_ARG
+    assert L.moe_expert_prefetch(ctypes.byref(d), FAKE, None, 10, FAKE, 1 << 20, None) == m.MOE_ERR_ARG
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert m.lib.moe_status_string(s)
