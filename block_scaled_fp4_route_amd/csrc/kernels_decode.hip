@@ -610,7 +610,11 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
 // chunks c = l + 64m (32 codes each), so every load instruction reads 1 KB
 // of one row contiguously, and the wave keeps the activations of its chunks
 // (x, or one hidden vector) in registers for every row it reads.
-constexpr int kStreamDP = 4;  // gate/up row pairs in flight per wave
+// gate/up row pairs in flight per wave: 3 for moe_expert_decode, 2 for the
+// layer form (whose top-k runs first); measured at the DeepSeek shape, where
+// 4 and 6 were slower (more registers, fewer resident waves)
+template <bool TOPK>
+constexpr int stream_dp() { return TOPK ? 2 : 3; }
 constexpr int kStreamRows = 8;  // down rows per workgroup
 
 __device__ __forceinline__ uint32_t ld_b16(rsrc_t r, uint32_t off) {
@@ -681,7 +685,7 @@ __device__ __forceinline__ void consume(uint32_t v) { asm volatile("" ::"v"(v));
 // row of one routed slot) are split into contiguous ranges, one per
 // workgroup of the grid (sized to be resident at once); wave w takes units
 // w, w + 4, ... of its workgroup's range, so the four waves sweep adjacent
-// rows together, and keeps kStreamDP units of loads in flight. The scales
+// rows together, and keeps stream_dp<TOPK>() units of loads in flight. The scales
 // of a unit come with one dword per lane (MXFP4: lanes 0-31 the gate row's,
 // 32-63 the up row's; NVFP4: one dword of each row) and reach the lanes that
 // need them by ds_bpermute. TOPK (moe_layer_decode): the workgroup first
@@ -692,7 +696,7 @@ __device__ __forceinline__ void consume(uint32_t v) { asm volatile("" ::"v"(v));
 template <int FMT, int NCH, bool TOPK>
 __global__ __launch_bounds__(256) void k_gateup_stream(DecodeArgs a) {
     constexpr int G = Fmt<FMT>::G;
-    constexpr int DP = kStreamDP;
+    constexpr int DP = stream_dp<TOPK>();
     constexpr int NSC = FMT == kFmtNvfp4 ? 2 : 1;  // scale dwords per lane per unit
     __shared__ const void* blks[kMaxK];
     const int lane = threadIdx.x & 63, wave = wave_id();
