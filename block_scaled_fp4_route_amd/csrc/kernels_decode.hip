@@ -615,7 +615,7 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
 // 4 and 6 were slower (more registers, fewer resident waves)
 template <bool TOPK>
 constexpr int stream_dp() { return TOPK ? 2 : 3; }
-constexpr int kStreamRows = 8;  // down rows per workgroup
+constexpr int kStreamRows = 16;  // down rows per workgroup
 
 __device__ __forceinline__ uint32_t ld_b16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
