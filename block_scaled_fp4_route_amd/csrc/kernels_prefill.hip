@@ -1093,9 +1093,9 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         gd.a_scl_bytes = (uint32_t)((size_t)n * I / 32);
         gd.NT = H / 64;
         if (2 * I <= 8192)
-            hipLaunchKernelGGL((k_mx_stream<false, 256, 4, 8192>), dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+            hipLaunchKernelGGL((k_mx_stream<false, 256, 3, 8192>), dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         else
-            hipLaunchKernelGGL((k_mx_stream<false, 256, 4, 32768>), dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+            hipLaunchKernelGGL((k_mx_stream<false, 256, 3, 32768>), dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     }
     hipLaunchKernelGGL(k_combine_prefill, dim3((H / 4 + 255) / 256, T), dim3(256), 0, s, L.Y, L.pos, w, k, H, out,
