@@ -31,6 +31,7 @@ namespace moe {
 
 constexpr int kMaxI = 4096;
 constexpr int kDownRB = 8;  // output rows per down workgroup
+constexpr int kDownNJ = 1;  // routed items per wave in the down launch (16-lane rows)
 
 // Workspace regions after the reserved bytes: h [(k+1)][I], logits [E],
 // chosen block addresses [k], shared-expert down rows [H].
@@ -567,16 +568,23 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
     if (tid < k) wsh[tid] = a.w[tid];
     const float ysh_row = (a.ysh != nullptr && tid < kDownRB) ? a.ysh[rb * kDownRB + tid] : 0.f;
     if constexpr (PAIRS) {
-        // one unit per wave: routed items in pairs (items w and w + npair),
-        // then the two halves of the shared expert's rows; the wave's two LDS
-        // slices hold the hidden vectors
-        const int npair = (k + 1) / 2;
-        f4v* hs = hsm + (size_t)wave * 2 * (a.I / 4);
+        // one unit per wave: kDownNJ routed items (items w, w + npair, ...),
+        // then the two halves of the shared expert's rows; the wave's kDownNJ
+        // LDS slices hold the hidden vectors
+        constexpr int NJ = kDownNJ;
+        const int npair = (k + NJ - 1) / NJ;
+        f4v* hs = hsm + (size_t)wave * NJ * (a.I / 4);
         if (wave < npair) {
-            int sl[2] = {wave, wave + npair < k ? wave + npair : -1};
-            const void* bl[2] = {a.sel[sl[0]], sl[1] >= 0 ? a.sel[sl[1]] : nullptr};
-            float* const dd[2] = {part[sl[0]], part[max(sl[1], 0)]};
-            down_items16<FMT, DD, 2>(a, sl, bl, rb, dd, hs);
+            int sl[NJ];
+            const void* bl[NJ];
+            float* dd[NJ];
+#pragma unroll
+            for (int i = 0; i < NJ; i++) {
+                sl[i] = wave + i * npair < k ? wave + i * npair : -1;
+                bl[i] = sl[i] >= 0 ? a.sel[sl[i]] : nullptr;
+                dd[i] = part[max(sl[i], 0)];
+            }
+            down_items16<FMT, DD, NJ>(a, sl, bl, rb, dd, hs);
         } else if (SH) {
             down_item<FMT, DL, DD, true, true>(a, k, nullptr, rb, (wave - npair) * (PASSES / 2), PASSES / 2,
                                                part[k], hs);
@@ -948,13 +956,13 @@ template <int FMT>
 static hipError_t launch_down(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
     const bool sh = a.n_items > a.k;
     const int maxw = down_max_waves(p.down_L, p.down_D);
-    const int units = (a.k + 1) / 2 + (a.n_items - a.k);  // routed pairs + shared halves
+    const int units = (a.k + kDownNJ - 1) / kDownNJ + (a.n_items - a.k);  // routed units + shared halves
     const bool pairs = p.down_L == 16 && units <= maxw;
     const int nw = pairs ? units : min(maxw, a.n_items);
     dim3 grid(a.H / kDownRB), block(64 * nw);
     // hidden vectors in LDS for 16-lane rows: two I-float slices per wave
     // (pairs), one otherwise
-    const size_t shm = p.down_L == 16 ? (size_t)nw * (pairs ? 2 : 1) * a.I * sizeof(float) : 0;
+    const size_t shm = p.down_L == 16 ? (size_t)nw * (pairs ? kDownNJ : 1) * a.I * sizeof(float) : 0;
 #define DNV(DL, DD, SH, PR) hipLaunchKernelGGL((k_down_combine<FMT, DL, DD, SH, PR>), grid, block, shm, s, a)
 #define DN(DL, DD)                                                   \
     case DD:                                                         \
