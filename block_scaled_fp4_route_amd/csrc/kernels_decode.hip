@@ -919,6 +919,101 @@ __global__ __launch_bounds__(64 * 8) void k_down_stream(DecodeArgs a) {
     }
 }
 
+// The same launch for rows of 65 to 96 chunks (2048 < I <= 3072). Each row's
+// first 64 chunks take one load across the wave; the remaining chunks (at
+// most 32) of two neighbouring rows share one load, lanes 0-31 the first
+// row's and lanes 32-63 the second's. Two rows then cost three loads and
+// three chunk products per lane instead of four (a quarter of the general
+// form's lanes idle at I = 2880).
+template <int FMT>
+__global__ __launch_bounds__(64 * 8) void k_down_stream_pair(DecodeArgs a) {
+    constexpr int G = Fmt<FMT>::G;
+    constexpr int R = kStreamRows;
+    constexpr int SCB = R * 3072 / G;  // scale bytes of R rows, I <= 3072
+    __shared__ float part[8][R];
+    __shared__ float wsh[8];
+    __shared__ __attribute__((aligned(16))) uint8_t scs[8][SCB];
+    const int tid = threadIdx.x, lane = tid & 63, j = wave_id();
+    const int H = a.H, I = a.I, k = a.k;
+    const int nchunk = I / 32, ntail = nchunk - 64;  // 1 .. 32
+    const int hi = lane >> 5, tl = lane & 31;
+    const int ct = min(64 + tl, nchunk - 1);  // this lane's tail chunk (clamped)
+    const uint32_t KB = (uint32_t)I / 2, KS = (uint32_t)I / G;
+    const uint32_t codes0 = (uint32_t)I * H;
+    const uint32_t scl0 = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / G;
+    const int n0 = blockIdx.x * R;
+    const void* blk = uniform_ptr(a.sel[j]);
+    const bool bad = blk == nullptr;
+    const rsrc_t rs = make_rsrc(bad ? (const void*)a.x : blk, bad ? 0u : a.block_bytes);
+    uint4 cw[R], cwt[R / 2];
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, codes0 + (uint32_t)(n0 + q) * KB + 16u * lane, 0, kNT);
+        cw[q] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int p = 0; p < R / 2; p++) {
+        const uint32_t row = (uint32_t)(n0 + 2 * p + hi);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, sel_u32(tl < ntail, codes0 + row * KB + 16u * (64 + tl), kOOB), 0, kNT);
+        cwt[p] = uint4{v[0], v[1], v[2], v[3]};
+    }
+    constexpr int NSL = (SCB + 1023) / 1024;
+    uint4 sl[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; i++) {
+        const uint32_t o = 16u * (lane + 64 * i);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, sel_u32(o < R * KS, scl0 + n0 * KS + o, kOOB), 0, 0);
+        sl[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+    // activations of chunk lane (set 0) and of the tail chunk (set 1)
+    float hs[2][32];
+    {
+        const f4v* v4 = reinterpret_cast<const f4v*>(a.h + (size_t)j * I);
+        const int cc[2] = {lane, ct};
+#pragma unroll
+        for (int m = 0; m < 2; m++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const f4v t = v4[8 * cc[m] + i];
+                hs[m][4 * i] = t.x; hs[m][4 * i + 1] = t.y; hs[m][4 * i + 2] = t.z; hs[m][4 * i + 3] = t.w;
+            }
+    }
+    if (tid < k) wsh[tid] = a.w[tid];
+#pragma unroll
+    for (int i = 0; i < NSL; i++) {
+        const int o = 16 * (lane + 64 * i);
+        if (o < SCB) *reinterpret_cast<uint4*>(&scs[j][o]) = sl[i];
+    }
+    auto scale = [&](int q, int c) -> uint32_t {
+        const uint32_t so = (uint32_t)q * KS + (FMT == kFmtNvfp4 ? 2u * c : (uint32_t)c);
+        return FMT == kFmtNvfp4 ? *reinterpret_cast<const uint16_t*>(&scs[j][so]) : scs[j][so];
+    };
+    // (this wave's LDS writes and reads stay in order: no barrier needed)
+#pragma unroll
+    for (int p = 0; p < R / 2; p++) {
+        const int q0 = 2 * p, q1 = 2 * p + 1;
+        float acc0 = chunk_dot<FMT>(cw[q0], scale(q0, lane), hs[0], 0.f);
+        float acc1 = chunk_dot<FMT>(cw[q1], scale(q1, lane), hs[0], 0.f);
+        float t = chunk_dot<FMT>(cwt[p], scale(q0 + hi, ct), hs[1], 0.f);
+        t = tl < ntail ? t : 0.f;
+        acc0 += hi ? 0.f : t;
+        acc1 += hi ? t : 0.f;
+        acc0 = wave_sum(acc0);
+        acc1 = wave_sum(acc1);
+        if (lane == 0) {
+            part[j][q0] = bad ? __uint_as_float(0x7FC00000u) : acc0;
+            part[j][q1] = bad ? __uint_as_float(0x7FC00000u) : acc1;
+        }
+    }
+    __syncthreads();
+    if (tid < R) {
+        float acc = 0.f;
+        for (int jj = 0; jj < k; jj++) acc = fmaf(wsh[jj], part[jj][tid], acc);
+        a.y[n0 + tid] = acc;
+    }
+}
+
 // the stream forms serve layers with no shared expert, k <= 8, I % 64 == 0
 // and at least 32 MB of gate/up codes per token (H, I <= 4096 as for every
 // decode layer)
@@ -946,7 +1041,7 @@ static hipError_t launch_stream(DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(gu, dim3(grid), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto dn = nch_i == 1 ? k_down_stream<FMT, 1> : k_down_stream<FMT, 2>;
+    auto dn = nch_i == 1 ? k_down_stream<FMT, 1> : a.I <= 3072 ? k_down_stream_pair<FMT> : k_down_stream<FMT, 2>;
     hipLaunchKernelGGL(dn, dim3(a.H / kStreamRows), dim3(64 * a.k), 0, s, a);
     return hipGetLastError();
 }

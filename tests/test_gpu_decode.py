@@ -152,6 +152,11 @@ def test_decode_deterministic_reruns(m, orc):
     # streaming kernels: one 1 KB chunk per lane and row, 1.5 chunks, 2 chunks
     ("mxfp4", 2048, 2048, 10, 8),
     ("nvfp4", 3072, 1536, 9, 8),
+    # 65-96 chunks per down row: two rows share the load of their tails
+    # (2 tail chunks, 26 as at I = 2880, a full 32)
+    ("mxfp4", 2560, 2112, 8, 7),
+    ("mxfp4", 2048, 2880, 9, 6),
+    ("nvfp4", 2048, 3072, 8, 6),
 ])
 def test_decode_edge_shapes(m, orc, fmt, H, I, E, k):
     wl = sg.Workload("edge", 90, H, I, E, k, fmt, 1, 1, False, "router", 0.0,
