@@ -35,11 +35,11 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain 1 GiB copy gives),
 # per workload; absent until counters were taken on the current kernels.
 # qwen_decode: k_gateup<1,5,2> + k_down_combine<1,16,5,true,true>.
-# deepseek_decode: k_gateup_stream<2,2,false> + k_down_stream<2,2>.
+# deepseek_decode: k_gateup_stream<2,2,false> + k_down_stream_pair<2>.
 # deepseek_prefill: every kernel of one moe_expert_prefill call (group,
 # tile_list, quant_mx x2, k_mx_stream gate/up and down, combine).
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
-TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114139668, "deepseek_prefill": 7298292121, "fp8_act_quant": 21130606,
+TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114146438, "deepseek_prefill": 7298292121, "fp8_act_quant": 21130606,
                  "fp8_gemv": 21211008}
 
 
@@ -227,7 +227,7 @@ def run_decode(args, m, sg, torch):
     expert_call_bytes = experts + shared + act
     achieved = expert_call_bytes / (expert_us * 1e-6) / 1e9
     copy_gbps = measure_copy_bandwidth(torch)
-    pair = "k_gateup + k_down_combine" if wl.fmt == "nvfp4" else "k_gateup_stream + k_down_stream"
+    pair = "k_gateup + k_down_combine" if wl.fmt == "nvfp4" else "k_gateup_stream + k_down_stream_pair"
     res = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
