@@ -613,16 +613,18 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
 // Streaming forms for large layers. When the chosen experts' weights are
 // many times what one round of resident workgroups has in flight, the
 // one-shot tiles above run in several rounds, each paying the full memory
-// latency. Here a resident grid keeps loads in flight continuously instead.
+// latency. Here a resident grid (one workgroup of four waves per compute
+// unit: a wave per SIMD) keeps loads in flight continuously instead.
 // A wave covers a weight row with all 64 lanes: lane l reads the 16-byte
 // chunks c = l + 64m (32 codes each), so every load instruction reads 1 KB
 // of one row contiguously, and the wave keeps the activations of its chunks
 // (x, or one hidden vector) in registers for every row it reads.
-// gate/up row pairs in flight per wave: 3 for moe_expert_decode, 2 for the
-// layer form (whose top-k runs first); measured at the DeepSeek shape, where
-// 4 and 6 were slower (more registers, fewer resident waves)
+// gate/up row pairs in flight per wave: 4 for moe_expert_decode, 3 for the
+// layer form (whose top-k runs first). Measured at the DeepSeek shape: with
+// three workgroups per compute unit 2 and 3 did best (more cost registers and
+// resident waves); with one per compute unit 3 and 4 are 2% faster again.
 template <bool TOPK>
-constexpr int stream_dp() { return TOPK ? 2 : 3; }
+constexpr int stream_dp() { return TOPK ? 3 : 4; }
 constexpr int kStreamRows = 16;  // down rows per workgroup
 
 __device__ __forceinline__ uint32_t ld_b16(rsrc_t r, uint32_t off) {
@@ -691,7 +693,7 @@ __device__ __forceinline__ void consume(uint32_t v) { asm volatile("" ::"v"(v));
 
 // gate/up + SiLU*mul, streaming. Units u = slot * I + row (gate row and up
 // row of one routed slot) are split into contiguous ranges, one per
-// workgroup of the grid (sized to be resident at once); wave w takes units
+// workgroup of the grid (one per compute unit); wave w takes units
 // w, w + 4, ... of its workgroup's range, so the four waves sweep adjacent
 // rows together, and keeps stream_dp<TOPK>() units of loads in flight. The scales
 // of a unit come with one dword per lane (MXFP4: lanes 0-31 the gate row's,
@@ -1022,21 +1024,19 @@ static bool use_stream(const DecodeArgs& a) {
            a.I % 64 == 0;
 }
 
-// resident workgroups of a kernel: occupancy per CU times the CU count
-template <class KERNEL>
-static int resident_grid(KERNEL kern, int threads) {
-    int dev = 0, cus = 0, per = 0;
+// compute units of the current device (0 on error)
+static int cu_count() {
+    int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess) return 0;
-    return cus * per;
+    return cus;
 }
 
 template <int FMT, bool TOPK>
 static hipError_t launch_stream(DecodeArgs& a, hipStream_t s) {
     const int nch_h = (a.H / 32 + 63) / 64, nch_i = (a.I / 32 + 63) / 64;
     auto gu = nch_h == 1 ? k_gateup_stream<FMT, 1, TOPK> : k_gateup_stream<FMT, 2, TOPK>;
-    const int grid = resident_grid(gu, 256);
+    const int grid = cu_count();
     if (grid <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(gu, dim3(grid), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
