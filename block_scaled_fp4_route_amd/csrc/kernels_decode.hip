@@ -926,16 +926,20 @@ __global__ __launch_bounds__(64 * 8) void k_down_stream(DecodeArgs a) {
 // most 32) of two neighbouring rows share one load, lanes 0-31 the first
 // row's and lanes 32-63 the second's. Two rows then cost three loads and
 // three chunk products per lane instead of four (a quarter of the general
-// form's lanes idle at I = 2880).
-template <int FMT>
-__global__ __launch_bounds__(64 * 8) void k_down_stream_pair(DecodeArgs a) {
+// form's lanes idle at I = 2880). NH waves share a routed slot, each with
+// R / NH of the rows: with k <= 6, two per slot put three waves on every
+// SIMD instead of one or two (down 14.05 -> 13.44 us at the DeepSeek shape).
+template <int FMT, int NH>
+__global__ __launch_bounds__(NH == 2 ? 64 * 12 : 64 * 8) void k_down_stream_pair(DecodeArgs a) {  // NH = 2: k <= 6
     constexpr int G = Fmt<FMT>::G;
     constexpr int R = kStreamRows;
-    constexpr int SCB = R * 3072 / G;  // scale bytes of R rows, I <= 3072
+    constexpr int RW = R / NH;              // rows per wave
+    constexpr int SCB = RW * 3072 / G;      // scale bytes of RW rows, I <= 3072
     __shared__ float part[8][R];
     __shared__ float wsh[8];
-    __shared__ __attribute__((aligned(16))) uint8_t scs[8][SCB];
-    const int tid = threadIdx.x, lane = tid & 63, j = wave_id();
+    __shared__ __attribute__((aligned(16))) uint8_t scs[8 * NH][SCB];
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+    const int j = wv / NH, q0w = (wv % NH) * RW;  // routed slot, first row of this wave
     const int H = a.H, I = a.I, k = a.k;
     const int nchunk = I / 32, ntail = nchunk - 64;  // 1 .. 32
     const int hi = lane >> 5, tl = lane & 31;
@@ -943,18 +947,18 @@ __global__ __launch_bounds__(64 * 8) void k_down_stream_pair(DecodeArgs a) {
     const uint32_t KB = (uint32_t)I / 2, KS = (uint32_t)I / G;
     const uint32_t codes0 = (uint32_t)I * H;
     const uint32_t scl0 = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / G;
-    const int n0 = blockIdx.x * R;
+    const int n0 = blockIdx.x * R + q0w;  // this wave's first output row
     const void* blk = uniform_ptr(a.sel[j]);
     const bool bad = blk == nullptr;
     const rsrc_t rs = make_rsrc(bad ? (const void*)a.x : blk, bad ? 0u : a.block_bytes);
-    uint4 cw[R], cwt[R / 2];
+    uint4 cw[RW], cwt[RW / 2];
 #pragma unroll
-    for (int q = 0; q < R; q++) {
+    for (int q = 0; q < RW; q++) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, codes0 + (uint32_t)(n0 + q) * KB + 16u * lane, 0, kNT);
         cw[q] = uint4{v[0], v[1], v[2], v[3]};
     }
 #pragma unroll
-    for (int p = 0; p < R / 2; p++) {
+    for (int p = 0; p < RW / 2; p++) {
         const uint32_t row = (uint32_t)(n0 + 2 * p + hi);
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(
             rs, sel_u32(tl < ntail, codes0 + row * KB + 16u * (64 + tl), kOOB), 0, kNT);
@@ -965,7 +969,7 @@ __global__ __launch_bounds__(64 * 8) void k_down_stream_pair(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NSL; i++) {
         const uint32_t o = 16u * (lane + 64 * i);
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, sel_u32(o < R * KS, scl0 + n0 * KS + o, kOOB), 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, sel_u32(o < RW * KS, scl0 + n0 * KS + o, kOOB), 0, 0);
         sl[i] = uint4{v[0], v[1], v[2], v[3]};
     }
     // activations of chunk lane (set 0) and of the tail chunk (set 1)
@@ -985,15 +989,15 @@ __global__ __launch_bounds__(64 * 8) void k_down_stream_pair(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NSL; i++) {
         const int o = 16 * (lane + 64 * i);
-        if (o < SCB) *reinterpret_cast<uint4*>(&scs[j][o]) = sl[i];
+        if (o < SCB) *reinterpret_cast<uint4*>(&scs[wv][o]) = sl[i];
     }
     auto scale = [&](int q, int c) -> uint32_t {
         const uint32_t so = (uint32_t)q * KS + (FMT == kFmtNvfp4 ? 2u * c : (uint32_t)c);
-        return FMT == kFmtNvfp4 ? *reinterpret_cast<const uint16_t*>(&scs[j][so]) : scs[j][so];
+        return FMT == kFmtNvfp4 ? *reinterpret_cast<const uint16_t*>(&scs[wv][so]) : scs[wv][so];
     };
     // (this wave's LDS writes and reads stay in order: no barrier needed)
 #pragma unroll
-    for (int p = 0; p < R / 2; p++) {
+    for (int p = 0; p < RW / 2; p++) {
         const int q0 = 2 * p, q1 = 2 * p + 1;
         float acc0 = chunk_dot<FMT>(cw[q0], scale(q0, lane), hs[0], 0.f);
         float acc1 = chunk_dot<FMT>(cw[q1], scale(q1, lane), hs[0], 0.f);
@@ -1004,15 +1008,15 @@ __global__ __launch_bounds__(64 * 8) void k_down_stream_pair(DecodeArgs a) {
         acc0 = wave_sum(acc0);
         acc1 = wave_sum(acc1);
         if (lane == 0) {
-            part[j][q0] = bad ? __uint_as_float(0x7FC00000u) : acc0;
-            part[j][q1] = bad ? __uint_as_float(0x7FC00000u) : acc1;
+            part[j][q0w + q0] = bad ? __uint_as_float(0x7FC00000u) : acc0;
+            part[j][q0w + q1] = bad ? __uint_as_float(0x7FC00000u) : acc1;
         }
     }
     __syncthreads();
     if (tid < R) {
         float acc = 0.f;
         for (int jj = 0; jj < k; jj++) acc = fmaf(wsh[jj], part[jj][tid], acc);
-        a.y[n0 + tid] = acc;
+        a.y[blockIdx.x * R + tid] = acc;
     }
 }
 
@@ -1041,7 +1045,15 @@ static hipError_t launch_stream(DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(gu, dim3(grid), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto dn = nch_i == 1 ? k_down_stream<FMT, 1> : a.I <= 3072 ? k_down_stream_pair<FMT> : k_down_stream<FMT, 2>;
+    if (nch_i == 2 && a.I <= 3072) {
+        // two waves per routed slot (half its rows each) while that fits 12 waves
+        if (a.k <= 6)
+            hipLaunchKernelGGL((k_down_stream_pair<FMT, 2>), dim3(a.H / kStreamRows), dim3(128 * a.k), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_down_stream_pair<FMT, 1>), dim3(a.H / kStreamRows), dim3(64 * a.k), 0, s, a);
+        return hipGetLastError();
+    }
+    auto dn = nch_i == 1 ? k_down_stream<FMT, 1> : k_down_stream<FMT, 2>;
     hipLaunchKernelGGL(dn, dim3(a.H / kStreamRows), dim3(64 * a.k), 0, s, a);
     return hipGetLastError();
 }
