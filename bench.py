@@ -35,11 +35,11 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain 1 GiB copy gives),
 # per workload; absent until counters were taken on the current kernels.
 # qwen_decode: k_gateup<1,5,2> + k_down_combine<1,16,5,true,true>.
-# deepseek_decode: k_gateup_stream<2,2,false> + k_down_stream_pair<2>.
+# deepseek_decode: k_gateup_stream<2,2,false> + k_down_stream_pair<2,2>.
 # deepseek_prefill: every kernel of one moe_expert_prefill call (group,
 # tile_list, quant_mx x2, k_mx_stream gate/up and down, combine).
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
-TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114155801, "deepseek_prefill": 7298292121, "fp8_act_quant": 21130606,
+TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114413381, "deepseek_prefill": 7298292121, "fp8_act_quant": 21130606,
                  "fp8_gemv": 21211008}
 
 
