@@ -39,7 +39,7 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # deepseek_prefill: every kernel of one moe_expert_prefill call (group,
 # tile_list, quant_mx x2, k_mx_stream gate/up and down, combine).
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
-TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114413381, "deepseek_prefill": 7298292121, "fp8_act_quant": 21130606,
+TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114413381, "deepseek_prefill": 7298292121, "fp8_act_quant": 21131081,
                  "fp8_gemv": 21211008}
 
 

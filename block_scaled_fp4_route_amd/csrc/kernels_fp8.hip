@@ -36,7 +36,7 @@ namespace moe {
 // and stored as the byte X + 127 (0 for an all-zero block). The quotients
 // v * 2^-X are exact (2^-X is a normal fp32 power of two), clamped to +-448
 // and rounded to nearest even by v_cvt_pk_fp8_f32 (OCP E4M3FN on gfx950).
-constexpr int kQuantPer = 1;  // float4 pieces per thread (more measured slower)
+constexpr int kQuantPer = 2;  // float4 pieces per thread (1 and 4 measured slower)
 
 template <int LPB>
 __device__ __forceinline__ void quant_piece(const float4 v, size_t i, int rule, uint32_t* __restrict__ codes,
