@@ -758,3 +758,216 @@ int orc_moe_prefill(int fmt, int H, int I, int E, int k, int T, const float *x, 
     parallel_for(T, nthreads, prefill_token_task, &c);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Prefill, stage by stage                                                   */
+/*                                                                           */
+/* The same per-token definition as orc_moe_prefill, cut at the rounding     */
+/* point of h so that each stage can be checked on its own: the gate/up      */
+/* stage on a list of assignments, and the down projection + combine on a    */
+/* caller-given h~ (for instance the one the GPU rounded). Every expert      */
+/* matrix a stage needs is dequantised to fp32 once (the same exact values   */
+/* weight_at gives) and each output element is the same fp64 sum over the    */
+/* input index in increasing order, so the results equal orc_moe_prefill's   */
+/* bit for bit where the inputs are the same.                                */
+/* ------------------------------------------------------------------------ */
+
+/* Rows of n values through the activation rounding act (ACT_NONE, ACT_BF16:
+ * bf16 round-to-nearest-even, ACT_MXFP4: MXFP4 per 32 along the row),
+ * returned as the rounded values in fp64. */
+int orc_round_rows(int act, int rows, int n, const double *in, double *out)
+{
+    if (act == ACT_MXFP4 && n % 32)
+        return -1;
+    for (int64_t r = 0; r < rows; r++)
+        round_activation(act, in + r * n, n, out + r * n);
+    return 0;
+}
+
+/* One assignment to evaluate: its expert, its id a = t*k + j and the caller's
+ * output row. Workers take them sorted by (expert, id, row), so that each
+ * meets an expert in one run and dequantises its matrices once. */
+struct stage_item { int32_t e, a, row; };
+static int cmp_stage_item(const void *pa, const void *pb)
+{
+    const struct stage_item *x = pa, *y = pb;
+    if (x->e != y->e) return (x->e > y->e) - (x->e < y->e);
+    if (x->a != y->a) return (x->a > y->a) - (x->a < y->a);
+    return (x->row > y->row) - (x->row < y->row);
+}
+
+static struct stage_item *sorted_items(int n, const int32_t *ids, const int32_t *idx)
+{
+    struct stage_item *it = malloc(sizeof(*it) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; i++) {
+        it[i].e = idx[ids[i]];
+        it[i].a = ids[i];
+        it[i].row = i;
+    }
+    qsort(it, (size_t)n, sizeof(*it), cmp_stage_item);
+    return it;
+}
+
+struct stage_ctx {
+    int fmt, H, I, k, act, nparts, n, out_bf16;
+    const float *x;
+    const uint8_t *const *blocks;
+    const struct stage_item *items;
+    const double *h_in;              /* down stage: h~ [n][I] */
+    double *h_pre, *h_q, *gu, *agu;  /* hidden stage outputs, [n][...] */
+    double *y;                       /* down stage: [n][H] */
+};
+
+static void stage_hidden_worker(void *p, int64_t part)
+{
+    struct stage_ctx *c = p;
+    int H = c->H, I = c->I;
+    int64_t lo = (int64_t)c->n * part / c->nparts, hi = (int64_t)c->n * (part + 1) / c->nparts;
+    if (lo >= hi)
+        return;
+    int64_t off[7];
+    orc_layout(c->fmt, H, I, off);
+    float *Wg = malloc(sizeof(float) * (size_t)I * H), *Wu = malloc(sizeof(float) * (size_t)I * H);
+    double *xt = malloc(sizeof(double) * (size_t)H), *xq = malloc(sizeof(double) * (size_t)H);
+    double *h = malloc(sizeof(double) * (size_t)I);
+    int cur = -1;
+    for (int64_t i = lo; i < hi; i++) {
+        const struct stage_item *it = &c->items[i];
+        int t = it->a / c->k;
+        int64_t row = it->row;
+        if (it->e != cur) {
+            const uint8_t *b = c->blocks[it->e];
+            dequant_matrix(c->fmt, b + off[0], b + off[3], I, H, Wg);
+            dequant_matrix(c->fmt, b + off[1], b + off[4], I, H, Wu);
+            cur = it->e;
+        }
+        for (int q = 0; q < H; q++)
+            xt[q] = c->x[(int64_t)t * H + q];
+        round_activation(c->act, xt, H, xq);                 /* x~ */
+        for (int r = 0; r < I; r++) {
+            double g = 0.0, u = 0.0, ag = 0.0, au = 0.0;
+            const float *wg = Wg + (int64_t)r * H, *wu = Wu + (int64_t)r * H;
+            for (int q = 0; q < H; q++) {
+                double pg = (double)wg[q] * xq[q], pu = (double)wu[q] * xq[q];
+                g += pg;
+                u += pu;
+                ag += fabs(pg);
+                au += fabs(pu);
+            }
+            h[r] = silu(g) * u;                              /* h = silu(g) * u */
+            if (c->gu) {
+                c->gu[(row * 2 + 0) * I + r] = g;
+                c->gu[(row * 2 + 1) * I + r] = u;
+            }
+            if (c->agu) {
+                c->agu[(row * 2 + 0) * I + r] = ag;
+                c->agu[(row * 2 + 1) * I + r] = au;
+            }
+        }
+        memcpy(c->h_pre + row * I, h, sizeof(double) * (size_t)I);
+        if (c->h_q)
+            round_activation(c->act, h, I, c->h_q + row * I); /* h~ */
+    }
+    free(Wg); free(Wu); free(xt); free(xq); free(h);
+}
+
+static int check_ids(int n, const int32_t *ids, const int32_t *idx, int T, int k, int E)
+{
+    for (int i = 0; i < n; i++)
+        if (ids[i] < 0 || ids[i] >= (int64_t)T * k || idx[ids[i]] < 0 || idx[ids[i]] >= E)
+            return -1;
+    return 0;
+}
+
+/* The gate/up stage of prefill for n assignments ids[i] = t*k + j: with
+ * x~ = Q(x_t) and e = idx[t][j], h = silu(Wg_e x~) * (Wu_e x~) (fp64) into
+ * h_pre[i][I], and h~ = Q(h) into h_q[i][I] (may be NULL). gu (may be
+ * NULL) receives [i][0][I] = g and [i][1][I] = u; agu (may be NULL) the sums
+ * of the absolute values of the same products, sum_c |W[r][c] x~[c]|: the
+ * magnitude that bounds the rounding error of any finite-precision
+ * evaluation of that dot product. */
+int orc_prefill_stage_hidden(int fmt, int H, int I, int E, int k, int T, const float *x,
+                             const uint8_t *const *blocks, const int32_t *idx, int act, int n, const int32_t *ids,
+                             double *h_pre, double *h_q, double *gu, double *agu, int nthreads)
+{
+    int64_t off[7];
+    if (orc_layout(fmt, H, I, off) || k < 1 || k > E || n < 0 || check_ids(n, ids, idx, T, k, E))
+        return -1;
+    if (act == ACT_MXFP4 && (H % 32 || I % 32))
+        return -1;
+    struct stage_item *items = sorted_items(n, ids, idx);
+    int parts = nthreads < 1 ? 1 : (nthreads > n ? (n > 0 ? n : 1) : nthreads);
+    struct stage_ctx c = {fmt, H, I, k, act, parts, n, 0, x, blocks, items, NULL, h_pre, h_q, gu, agu, NULL};
+    parallel_for(parts, parts, stage_hidden_worker, &c);
+    free(items);
+    return 0;
+}
+
+static void stage_down_worker(void *p, int64_t part)
+{
+    struct stage_ctx *c = p;
+    int H = c->H, I = c->I;
+    int64_t lo = (int64_t)c->n * part / c->nparts, hi = (int64_t)c->n * (part + 1) / c->nparts;
+    if (lo >= hi)
+        return;
+    int64_t off[7];
+    orc_layout(c->fmt, H, I, off);
+    float *Wd = malloc(sizeof(float) * (size_t)H * I);
+    int cur = -1;
+    for (int64_t i = lo; i < hi; i++) {
+        const struct stage_item *it = &c->items[i];
+        if (it->e != cur) {
+            const uint8_t *b = c->blocks[it->e];
+            dequant_matrix(c->fmt, b + off[2], b + off[5], H, I, Wd);
+            cur = it->e;
+        }
+        const double *hq = c->h_in + (int64_t)it->row * I;
+        double *y = c->y + (int64_t)it->row * H;
+        for (int r = 0; r < H; r++) {
+            double acc = 0.0;
+            const float *wd = Wd + (int64_t)r * I;
+            for (int q = 0; q < I; q++)
+                acc += (double)wd[q] * hq[q];
+            y[r] = acc;                                      /* y_j = Wd_e h~_j */
+        }
+    }
+    free(Wd);
+}
+
+/* The down projection and combine of prefill on a given h~: for tokens
+ * t < T, out[t] = sum_j w[t][j] * Wd_e h_q[t][j] with e = idx[t][j] (fp64,
+ * j increasing), rounded to bf16 when out_bf16 is set (the value of the
+ * rounded bf16 is stored). h_q is [T][k][I] in token order: the rounded
+ * hidden vectors of some evaluation of the gate/up stage. */
+int orc_prefill_down_combine(int fmt, int H, int I, int E, int k, int T, const uint8_t *const *blocks,
+                             const int32_t *idx, const float *w, const double *h_q, int out_bf16, double *out,
+                             int nthreads)
+{
+    int64_t off[7];
+    if (orc_layout(fmt, H, I, off) || k < 1 || k > E || T < 0)
+        return -1;
+    int n = T * k;
+    int32_t *ids = malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    for (int a = 0; a < n; a++)
+        ids[a] = a;
+    if (check_ids(n, ids, idx, T, k, E)) {
+        free(ids);
+        return -1;
+    }
+    struct stage_item *items = sorted_items(n, ids, idx);
+    double *y = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * H);
+    int parts = nthreads < 1 ? 1 : (nthreads > n ? (n > 0 ? n : 1) : nthreads);
+    struct stage_ctx c = {fmt, H, I, k, ACT_NONE, parts, n, out_bf16, NULL, blocks, items, h_q, NULL, NULL, NULL, NULL, y};
+    parallel_for(parts, parts, stage_down_worker, &c);
+    for (int t = 0; t < T; t++)
+        for (int r = 0; r < H; r++) {
+            double acc = 0.0;
+            for (int j = 0; j < k; j++)
+                acc += (double)w[t * k + j] * y[((int64_t)t * k + j) * H + r];
+            out[(int64_t)t * H + r] = out_bf16 ? orc_bf16_value(orc_bf16_rne(acc)) : acc;
+        }
+    free(items);
+    free(ids);
+    free(y);
+    return 0;
+}

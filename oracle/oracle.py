@@ -63,6 +63,11 @@ def lib():
         L.orc_gemv_fp8.restype = None; L.orc_gemv_fp8.argtypes = [I32, I32, P, P, P, P]
         L.orc_moe_prefill.restype = I32
         L.orc_moe_prefill.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, I32, I32, P, P, P, I32]
+        L.orc_round_rows.restype = I32; L.orc_round_rows.argtypes = [I32, I32, I32, P, P]
+        L.orc_prefill_stage_hidden.restype = I32
+        L.orc_prefill_stage_hidden.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, I32, I32, P, P, P, P, P, I32]
+        L.orc_prefill_down_combine.restype = I32
+        L.orc_prefill_down_combine.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, I32, P, I32]
         _lib = L
     return _lib
 
@@ -236,6 +241,62 @@ def group(idx, E):
     if lib().orc_group(T, k, E, _p(idx), _p(count), _p(off), _p(perm)):
         raise ValueError("expert index out of range")
     return count, off, perm
+
+
+def _block_table(blocks, E, idx):
+    """Pointer table of E expert blocks (dict {expert: array} or [E, bytes])."""
+    keep = []
+    ptrs = (C.c_void_p * E)()
+    if isinstance(blocks, dict):
+        for e, b in blocks.items():
+            bb = _c(b, np.uint8); keep.append(bb); ptrs[e] = bb.ctypes.data
+    else:
+        bb = _c(blocks, np.uint8); keep.append(bb)
+        for e in range(E):
+            ptrs[e] = bb.ctypes.data + e * bb.shape[1]
+    for e in np.unique(idx):
+        if not ptrs[int(e)]:
+            raise ValueError(f"expert {e} is routed to but its block is missing")
+    return ptrs, keep
+
+
+def round_rows(act, v):
+    """Rows through the activation rounding (ACT_BF16 / ACT_MXFP4 / ACT_NONE), as fp64 values."""
+    v = _c(v, np.float64)
+    v2 = v.reshape(-1, v.shape[-1])
+    out = np.empty_like(v2)
+    if lib().orc_round_rows(int(act), v2.shape[0], v2.shape[1], _p(v2), _p(out)):
+        raise ValueError("row length must be a multiple of 32 for MXFP4")
+    return out.reshape(v.shape)
+
+
+def prefill_stage_hidden(fmt, H, I, E, x, blocks, idx, act, ids, nthreads=1):
+    """Gate/up stage of prefill for assignments ids (a = t*k + j).
+    -> h_pre [n,I], h_q [n,I], gu [n,2,I] (g, u), agu [n,2,I] (sum |W x~| of g and u)."""
+    x = _c(x, np.float32); idx = _c(idx, np.int32); ids = _c(ids, np.int32).reshape(-1)
+    T, k = idx.shape
+    ptrs, keep = _block_table(blocks, E, idx.reshape(-1)[ids] if ids.size else [])
+    n = ids.size
+    hp = np.empty((n, I)); hq = np.empty((n, I)); gu = np.empty((n, 2, I)); agu = np.empty((n, 2, I))
+    r = lib().orc_prefill_stage_hidden(fmt_id(fmt), H, I, E, k, T, _p(x), C.cast(ptrs, C.c_void_p), _p(idx),
+                                       int(act), n, _p(ids), _p(hp), _p(hq), _p(gu), _p(agu), nthreads)
+    if r:
+        raise ValueError("bad arguments")
+    return hp, hq, gu, agu
+
+
+def prefill_down_combine(fmt, H, I, E, blocks, idx, w, h_q, out_bf16=False, nthreads=1):
+    """Down projection + combine on a given h~ [T,k,I] (token order) -> out f64 [T,H]."""
+    idx = _c(idx, np.int32); w = _c(w, np.float32); hq = _c(h_q, np.float64)
+    T, k = idx.shape
+    assert hq.shape == (T, k, I), hq.shape
+    ptrs, keep = _block_table(blocks, E, idx)
+    out = np.empty((T, H), np.float64)
+    r = lib().orc_prefill_down_combine(fmt_id(fmt), H, I, E, k, T, C.cast(ptrs, C.c_void_p), _p(idx), _p(w),
+                                       _p(hq), int(out_bf16), _p(out), nthreads)
+    if r:
+        raise ValueError("bad arguments")
+    return out
 
 
 def moe_prefill(fmt, H, I, E, x, blocks, idx, w, act, out_bf16=False, want_h=False, nthreads=1):

@@ -389,5 +389,9 @@ def test_prefill_mxfp4_rounding_points(orc):
                 c2, s2 = orc.mxfp4_quant(hp[t, j, b0:b0 + 32])
                 ref = np.array([orc.e2m1(int(c)) for c in c2]) * orc.ue8m0(s2)
                 assert (hq[t, j, b0:b0 + 32] == ref).all()
-        ref_out = orc.bf16_value(orc.bf16_rne(acc))
-        assert (np.abs(out[t] - ref_out) <= 2 ** -7 * np.abs(ref_out) + 1e-30).all()
+        # bf16 out: round-to-nearest-even of the fp64 combine, bit for bit
+        # (independent bit-level rounding), except within 1e-12 relative of a
+        # bf16 midpoint, where numpy's summation order may round the other way
+        from test_oracle_stages import bf16_rne_bits, near_bf16_midpoint
+        ok = ~near_bf16_midpoint(acc, 1e-12)
+        assert np.array_equal(out[t][ok], bf16_rne_bits(acc[ok]))
