@@ -642,8 +642,8 @@ def main():
                     help="only run 4 device copies of 1 GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the library has no multi-GPU path; "
-              "it computes one GPU's share of the experts.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path, and each "
+              "step computes the whole MoE layer on that GPU.", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -693,8 +693,8 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // 4c. MXFP4 grouped GEMMs: v_mfma_scale_f32_16x16x128_f8f6f4 on the e2m1
-// codes of both operands with their UE8M0 block scales ([D] "Making it
-// faster": the FP4 weights go to the matrix cores as they are, never
+// codes of both operands with their UE8M0 block scales (a design choice of
+// this library: the FP4 weights go to the matrix cores as stored, never
 // widened). With a few tokens per expert these GEMMs stream the expert
 // weights once, so the kernel is built around reading weight rows the way
 // HBM likes best: whole row segments, contiguous.

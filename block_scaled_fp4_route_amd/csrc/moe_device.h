@@ -163,7 +163,11 @@ __device__ __forceinline__ float key_f32(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g / (1 + e^-g) * u. expf, not __expf: the fast form rounds
+// -g * log2(e) to fp32 before the hardware exp2, a relative error of about
+// |g| * 2^-24 in e^-g (1e-6 at g = -20); expf keeps it to a few ulp. For
+// g < -ln(FLT_MAX) e^-g overflows and the result is +-0.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 constexpr int kTopkMaxE = 1024;
 

@@ -130,7 +130,11 @@ size_t moe_workspace_bytes(const moe_desc *d, int32_t T, int32_t mode);
  *   Wr         [E][H] fp32, 16-B aligned
  *   idx        [T][k] int32 (out);  w [T][k] fp32 (out)
  *   logits_out [T][E] fp32 (out) or NULL
- * Requires H % 4 == 0, E <= 1024, k <= min(E, 32). */
+ * Errors: MOE_ERR_ARG for an invalid descriptor (k > E, sizes not positive
+ * or not multiples of G), a null or misaligned pointer, T < 1;
+ * MOE_ERR_UNSUPPORTED unless H % 256 == 0, H <= 8192, E <= 1024 and k <= 32;
+ * MOE_ERR_WORKSPACE for a workspace below moe_workspace_bytes(d, T,
+ * MOE_MODE_ROUTE). */
 int moe_route(const moe_desc *d, const float *x, int32_t T, const float *Wr, int32_t *idx, float *w,
               float *logits_out, void *ws, size_t ws_bytes, void *stream);
 
@@ -138,7 +142,11 @@ int moe_route(const moe_desc *d, const float *x, int32_t T, const float *Wr, int
 /* Decode: one token                                                       */
 /* ---------------------------------------------------------------------- */
 
-/* y = sum_{j<k} w[j] * expert_{idx[j]}(x)  (+ shared(x) if shared != NULL)
+/* The single-token expert computation of one MoE layer ([Q] "The engine",
+ * item 4: a single-token SwiGLU expert kernel over NVFP4 weights, decoding
+ * the e2m1 codes on the fly; [Q] "Why this model, of all models": gate, up
+ * and down matrices per expert, and a shared expert kept in bf16):
+ * y = sum_{j<k} w[j] * expert_{idx[j]}(x)  (+ shared(x) if shared != NULL)
  * where expert_e(x) = down_e( silu(gate_e x) * (up_e x) ), silu(z) =
  * z / (1 + exp(-z)), weights decoded on the fly from the block at
  * expert_ptrs[e] (format per d->format), fp32 activations and fp32

@@ -221,6 +221,65 @@ def test_route_exact_logits_with_ties(m, orc, T):
     assert rel_err(gw, ow) <= TOL
 
 
+@pytest.mark.parametrize("T", [1, 17, 40])
+@pytest.mark.parametrize("E,k", [(128, 10), (256, 8), (384, 6), (512, 10), (1024, 32)])
+def test_topk_bitexact_from_gpu_logits(m, orc, E, k, T):
+    """Given the GPU's own fp32 logits, the GPU's chosen experts equal the
+    oracle's sort-based top-k bit for bit (lane counts of 2, 4, 6, 8 and 16
+    logits per lane), and its weights match the softmax over those logits
+    renormalised over the chosen k."""
+    from scipy.special import softmax
+    H = 2560 if E != 384 else 4096
+    wl = sg.Workload("topk", 93, H, 640, E, k, "nvfp4", 1, 1, False, "router", 0.0, 0x18, 0x48, False)
+    d = m.desc(H, 640, E, k, "nvfp4")
+    Wr = sg.router_weights(wl, 0, device="cuda")
+    x = sg.activations(wl, 3, 0, T=T, device="cuda")
+    gi, gw, gl = _route_gpu(m, d, x, Wr, T)
+    for t in range(T):
+        l = gl[t].astype(np.float64)
+        oi = orc.topk_sort(l, k)
+        assert (gi[t] == oi).all(), (t, gi[t], oi)
+        p = softmax(l)
+        assert rel_err(gw[t], p[oi] / p[oi].sum()) <= TOL
+
+
+@pytest.mark.parametrize("path", ["route", "layer"])
+def test_exact_logits_with_ties_at_512_experts(m, orc, path):
+    """512 experts (eight logits per lane, sort network + lane shifts) with
+    integer router weights and activations: exact logits, planted duplicate
+    rows across lanes and within one lane; moe_route and moe_layer_decode
+    must both pick the oracle's experts bit for bit."""
+    H, I, E, k = 2560, 640, 512, 10
+    d = m.desc(H, I, E, k, "nvfp4")
+    g = torch.Generator().manual_seed(512)
+    Wr = torch.randint(-3, 4, (E, H), generator=g).float()
+    x = torch.randint(-2, 3, (H,), generator=g).float()
+    lg = (Wr @ x).numpy()
+    top = int(np.argsort(-lg, kind="stable")[0])
+    dups = [v for v in (3, 4, 5, 200, 201, 511) if v != top][:5]
+    for dup in dups:                            # ties with the best row: same lane and other lanes
+        Wr[dup] = Wr[top]
+    Wr[100] = Wr[17]
+    lx = (Wr @ x).numpy()
+    if path == "route":
+        gi, gw, gl = _route_gpu(m, d, x[None].cuda(), Wr.cuda(), 1)
+        assert (gl[0] == orc.logits(x.numpy(), Wr.numpy())[0]).all()
+        gi = gi[0]
+    else:
+        wl = sg.Workload("ties512", 94, H, I, E, k, "nvfp4", 1, 1, False, "router", 0.0, 0x18, 0x48, False)
+        blocks = layer_blocks(wl, 0)
+        ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+        y = torch.empty(H, dtype=torch.float32, device="cuda")
+        idx = torch.empty(k, dtype=torch.int32, device="cuda")
+        w = torch.empty(k, dtype=torch.float32, device="cuda")
+        m.moe_layer_decode(d, x.cuda(), Wr.cuda(), m.expert_ptr_table(blocks), None, y, idx, w, ws)
+        torch.cuda.synchronize()
+        gi = idx.cpu().numpy()
+    _, oi, _ = orc.route(x.numpy()[None], Wr.numpy(), k)
+    assert (gi == oi[0]).all(), (gi, oi[0])
+    assert (lx[gi[:6]] == lx[top]).all()        # the planted ties are among the chosen
+
+
 def test_one_workspace_across_layers_and_calls(m, orc):
     """Route and decode of several layers share one workspace (its reserved
     first 4096 bytes are never written); each layer matches the oracle."""

@@ -6,6 +6,8 @@ result bit for bit (the kernels have no float atomics, and the library
 records no memset into a graph). One decode layer of the captured graph is
 also checked against the oracle.
 """
+import hashlib
+
 import numpy as np
 import pytest
 import torch
@@ -88,6 +90,69 @@ def test_decode_layers_in_a_graph(m, orc):
     ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, xs[l].cpu().numpy(), [hb[int(e)] for e in gi], ow[0],
                             shared=[bf16_bits(s) for s in shared[l]], nthreads=NTHREADS)
     assert rel_err(ys[l].cpu().numpy(), ref) <= 1e-4
+
+
+def test_48_layer_decode_graph_replays_identical(m, orc):
+    """The benchmark's configuration: all 48 Qwen-shaped layers (512 NVFP4
+    experts each, 63.3 GiB resident) + the bf16 shared experts through
+    moe_layer_decode on one workspace, captured in one HIP graph. Five
+    replays, with unrelated eager work between them, give identical outputs,
+    routing and weights in every layer (a hash of all 48 layers' results per
+    replay), equal to the eager run; the last layer matches the oracle.
+    A race between layers that share the workspace would show up as a
+    changed hash."""
+    wl = sg.get("qwen_decode")
+    L = wl.layers
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    blocks = torch.empty((L * wl.E, wl.block_bytes), dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        sg.fill_layer_blocks(wl, l, blocks[l * wl.E:(l + 1) * wl.E])
+    ptrs = [m.expert_ptr_table(blocks[l * wl.E:(l + 1) * wl.E]) for l in range(L)]
+    Wr = [sg.router_weights(wl, l, device="cuda") for l in range(L)]
+    shared = [[t.contiguous() for t in sg.shared_expert(wl, l, device="cuda")] for l in range(L)]
+    xs = [sg.activations(wl, 21, l, T=1, device="cuda").view(-1) for l in range(L)]
+    ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+    ys = torch.empty((L, wl.H), device="cuda")
+    idx = torch.empty((L, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, wl.k), device="cuda")
+
+    def run():
+        for l in range(L):
+            m.moe_layer_decode(d, xs[l], Wr[l], ptrs[l], shared[l], ys[l], idx[l], w[l], ws)
+
+    def digest():
+        h = hashlib.sha256()
+        for t in (ys, idx, w):
+            h.update(t.cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    try:
+        run()
+        torch.cuda.synchronize()
+        eager = digest()
+        g = capture(run)
+        seen = []
+        for rep in range(5):
+            ys.fill_(float("nan"))
+            idx.fill_(-1)
+            w.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            seen.append(digest())
+            eager_noise()
+        print(f"48-layer graph: eager {eager[:16]}, replays {[s[:16] for s in seen]}")
+        assert all(s == eager for s in seen), seen
+        l = L - 1
+        _, oi, ow = orc.route(xs[l].cpu().numpy(), Wr[l].cpu().numpy(), wl.k)
+        gi = idx[l].cpu().numpy()
+        assert (gi == oi[0]).all()
+        hb = host_blocks(blocks[l * wl.E:(l + 1) * wl.E], gi)
+        ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, xs[l].cpu().numpy(), [hb[int(e)] for e in gi], ow[0],
+                                shared=[bf16_bits(s) for s in shared[l]], nthreads=NTHREADS)
+        assert rel_err(ys[l].cpu().numpy(), ref) <= 1e-4
+    finally:
+        del blocks
+        torch.cuda.empty_cache()
 
 
 def test_fp8_kernels_in_a_graph(m, orc):

@@ -2,13 +2,13 @@
 an XOR checksum of every 64 KiB chunk of each guessed expert's block, which
 must equal numpy's XOR of the same words (so every byte was read); skipped
 indices give zeros. A decode layer running next to a prefetch on a second
-stream is bit-identical to one running alone."""
+stream is bit-identical to one running alone, and both match the oracle."""
 import numpy as np
 import pytest
 import torch
 
 import synthgen as sg
-from gpu_helpers import layer_blocks
+from gpu_helpers import NTHREADS, host_blocks, layer_blocks, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,7 @@ def test_prefetch_checksums(m, name, E):
         assert (got[j] == want).all(), (j, e)
 
 
-def test_prefetch_beside_decode_changes_nothing(m):
+def test_prefetch_beside_decode_changes_nothing(m, orc):
     wl = sg.get("qwen_layer_decode")
     E = 64
     blocks = layer_blocks(wl, 0, E=E)
@@ -70,3 +70,10 @@ def test_prefetch_beside_decode_changes_nothing(m):
     m.moe_layer_decode(d, x, Wr, ptrs, None, y1, i1, w1, ws)
     torch.cuda.synchronize()
     assert torch.equal(i0, i1) and torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    # the decode that ran beside the prefetch against the oracle
+    _, oi, ow = orc.route(x.cpu().numpy(), Wr.cpu().numpy(), wl.k)
+    gi = i1.cpu().numpy()
+    assert (gi == oi[0]).all()
+    hb = host_blocks(blocks, gi)
+    ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x.cpu().numpy(), [hb[int(e)] for e in gi], ow[0], nthreads=NTHREADS)
+    assert rel_err(y1.cpu().numpy(), ref) <= 1e-4

@@ -8,12 +8,17 @@ slot cache, and the per-layer pointer tables the decode kernels read.
   HBM-resident decode; afterwards every table entry points at its slot or at
   its host block, and every slot holds its expert's block.
 * A hand-worked routing sequence checks the LRU choice of victims.
+* Several decode steps and tier updates enqueued back to back with no host
+  synchronisation between them (so slots are overwritten while kernels that
+  read the old entries may still be queued) stay bit-identical to the
+  HBM-resident decode, step by step; tier decode matches the oracle.
 """
 import numpy as np
 import pytest
 import torch
 
 import synthgen as sg
+from gpu_helpers import NTHREADS, bf16_bits, host_blocks, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -149,5 +154,53 @@ def test_lru_victims_hand_worked(m):
             assert tab[e] == want, e
             if s >= 0:
                 assert (sl[s] == host.numpy()[e]).all(), e
+    finally:
+        tier.close()
+
+
+def test_tier_steps_without_host_sync(m, orc):
+    """Eight steps of two layers, each followed by a tier update, all
+    enqueued on one stream with no host synchronisation between them: the
+    routing each update receives was computed beforehand by a resident
+    decode of the same inputs (the tier never changes results, so it is the
+    routing the step itself produces). Every step's output is then compared
+    bit for bit with the resident decode, and one tier step with the oracle."""
+    wl = sg.get("qwen_layer_decode")
+    L, E, n_slots, S = 2, 64, 12, 8
+    d, tier, dev, host, slots, table, Wr, shared, ref_ptrs = make_tier(m, wl, E, L, n_slots, True)
+    try:
+        ws = m.alloc_workspace(d, 1, m.MOE_MODE_DECODE)
+        xs = [[sg.activations(wl, 40 + s, l, T=1, device="cuda").view(-1) for l in range(L)] for s in range(S)]
+
+        def outputs():
+            return (torch.empty((S, L, wl.H), device="cuda"), torch.empty((S, L, wl.k), dtype=torch.int32, device="cuda"),
+                    torch.empty((S, L, wl.k), device="cuda"))
+
+        ry, ri, rw = outputs()
+        for s in range(S):
+            for l in range(L):
+                m.moe_layer_decode(d, xs[s][l], Wr[l], ref_ptrs[l], shared[l], ry[s, l], ri[s, l], rw[s, l], ws)
+        torch.cuda.synchronize()
+        routing = ri.cpu().numpy()
+        ty, ti, tw = outputs()
+        for s in range(S):
+            for l in range(L):
+                m.moe_layer_decode(d, xs[s][l], Wr[l], tier.table(l), shared[l], ty[s, l], ti[s, l], tw[s, l], ws)
+            tier.update(routing[s], 8)   # no synchronisation: copies overlap the next step's kernels
+        torch.cuda.synchronize()
+        st = tier.stats()
+        assert st["promotions"] > 0 and st["evictions"] > 0, st
+        assert torch.equal(ti, ri)
+        assert torch.equal(ty.view(torch.int32), ry.view(torch.int32))
+        # one tier step against the oracle
+        s, l = S - 1, 1
+        x = xs[s][l].cpu().numpy()
+        _, oi, ow = orc.route(x, Wr[l].cpu().numpy(), wl.k)
+        gi = ti[s, l].cpu().numpy()
+        assert (gi == oi[0]).all()
+        hb = host_blocks(dev[l * E:(l + 1) * E], gi)
+        ref, _ = orc.moe_decode(wl.fmt, wl.H, wl.I, x, [hb[int(e)] for e in gi], ow[0],
+                                shared=[bf16_bits(t) for t in shared[l]], nthreads=NTHREADS)
+        assert rel_err(ty[s, l].cpu().numpy(), ref) <= 1e-4
     finally:
         tier.close()
