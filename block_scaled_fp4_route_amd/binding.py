@@ -18,11 +18,12 @@ MOE_FMT_NVFP4, MOE_FMT_MXFP4 = 1, 2
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = 0, -1, -2, -3, -4
 MOE_MODE_ROUTE, MOE_MODE_DECODE, MOE_MODE_PREFILL = 0, 1, 2
 MOE_OUT_F32, MOE_OUT_BF16 = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 1 << 20
 FORMATS = {"nvfp4": MOE_FMT_NVFP4, "mxfp4": MOE_FMT_MXFP4}
 
 # every symbol declared in include/moe_fp4.h
 EXPORTS = ("moe_block_bytes", "moe_block_layout", "moe_workspace_bytes", "moe_route", "moe_expert_decode",
-           "moe_layer_decode", "moe_expert_prefill", "moe_dequant_block", "moe_act_quant_fp8", "moe_gemv_fp8",
+           "moe_layer_decode", "moe_layer_decode_noalloc", "moe_expert_prefill", "moe_dequant_block", "moe_act_quant_fp8", "moe_gemv_fp8",
            "moe_prefetch_sink_bytes", "moe_expert_prefetch", "moe_tier_create", "moe_tier_destroy", "moe_tier_update", "moe_tier_get_stats", "moe_tier_slot_of",
            "moe_status_string", "moe_last_error")
 
@@ -71,6 +72,8 @@ def _load():
     L.moe_expert_decode.argtypes = [D, P, P, P, P, C.POINTER(moe_shared), P, P, SZ, P]
     L.moe_layer_decode.restype = C.c_int
     L.moe_layer_decode.argtypes = [D, P, P, P, C.POINTER(moe_shared), P, P, P, P, SZ, P]
+    L.moe_layer_decode_noalloc.restype = C.c_int
+    L.moe_layer_decode_noalloc.argtypes = [D, P, P, P, C.POINTER(moe_shared), P, P, P, P]
     L.moe_expert_prefill.restype = C.c_int
     L.moe_expert_prefill.argtypes = [D, P, I32, P, P, P, P, I32, P, SZ, C.POINTER(moe_prefill_debug), P]
     L.moe_dequant_block.restype = C.c_int; L.moe_dequant_block.argtypes = [D, P, P, P, P, P]
@@ -154,6 +157,15 @@ def moe_layer_decode(d, x, Wr, expert_ptrs, shared, y, idx_out, w_out, ws, ws_by
     wsb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check(lib.moe_layer_decode(C.byref(d), _ptr(x), _ptr(Wr), _ptr(expert_ptrs), sh, _ptr(y), _ptr(idx_out),
                                 _ptr(w_out), _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_layer_decode_noalloc(d, x, Wr, expert_ptrs, shared, y, idx_out, w_out, stream=None):
+    """moe_layer_decode with the library's static scratch as its workspace."""
+    sh = None
+    if shared is not None:
+        sh = C.byref(moe_shared(_ptr(shared[0]), _ptr(shared[1]), _ptr(shared[2])))
+    _check(lib.moe_layer_decode_noalloc(C.byref(d), _ptr(x), _ptr(Wr), _ptr(expert_ptrs), sh, _ptr(y), _ptr(idx_out),
+                                        _ptr(w_out), _stream(stream)))
 
 
 def moe_expert_prefill(d, x, T, expert_ptrs, idx, w, out, out_dtype, ws, ws_bytes=None, dbg=None, stream=None):

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -140,9 +141,13 @@ int moe_expert_decode(const moe_desc* d, const float* x, const void* const* expe
                       "decode launch");
 }
 
-int moe_layer_decode(const moe_desc* d, const float* x, const float* Wr, const void* const* expert_ptrs,
-                     const moe_shared* shared, float* y, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every argument check of moe_layer_decode except the workspace.
+int layer_decode_checks(const moe_desc* d, const float* x, const float* Wr, const void* const* expert_ptrs,
+                        const moe_shared* shared, float* y, int32_t* idx_out, float* w_out, moe::DecodePlan* plan) {
     int r;
     if ((r = check_desc(d))) return r;
     if ((r = check_ptr(x, 16, "x")) || (r = check_ptr(Wr, 16, "Wr")) || (r = check_ptr(expert_ptrs, 8, "expert_ptrs")) ||
@@ -156,16 +161,77 @@ int moe_layer_decode(const moe_desc* d, const float* x, const float* Wr, const v
     if (!moe::route_supported(d->H, d->E, d->k))
         return fail(MOE_ERR_UNSUPPORTED, "router needs H %% 256 == 0, H <= 8192, E <= %d, k <= %d (H=%d E=%d k=%d)",
                     moe::kMaxE, moe::kMaxK, d->H, d->E, d->k);
-    moe::DecodePlan plan;
-    if (!moe::plan_decode(d->format, d->H, d->I, &plan))
+    if (!moe::plan_decode(d->format, d->H, d->I, plan))
         return fail(MOE_ERR_UNSUPPORTED, "no decode kernel for H=%d I=%d (needs H %% 512 == 0, H <= 4096, I <= 4096)",
                     d->H, d->I);
-    if ((r = check_ws(ws, ws_bytes, moe::decode_ws_bytes(d->H, d->I, d->k, d->E)))) return r;
+    return MOE_OK;
+}
+
+int layer_decode_launch(const moe_desc* d, const moe::DecodePlan& plan, const float* x, const float* Wr,
+                        const void* const* expert_ptrs, const moe_shared* shared, float* y, int32_t* idx_out,
+                        float* w_out, void* ws, void* stream) {
     return hip_status(moe::launch_layer_decode(d->format, plan, d->E, d->H, d->I, d->k, x, Wr, expert_ptrs,
                                                shared ? shared->gate : nullptr, shared ? shared->up : nullptr,
                                                shared ? shared->down : nullptr, y, idx_out, w_out, ws,
                                                reinterpret_cast<hipStream_t>(stream)),
                       "layer decode launch");
+}
+
+// ---- the allocation-free decode ----
+// Its workspace: one copy of this array on every GPU the library runs on,
+// loaded with the library's code object (zero-filled) and held until the
+// process ends. In host code the name stands for a host-side shadow, not a
+// device address: only the address hipGetSymbolAddress returns for the
+// current device may reach a kernel.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // device address of scratch, per device, once looked up
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device; a lookup by two threads at once stores the same value).
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_decode(const moe_desc* d, const float* x, const float* Wr, const void* const* expert_ptrs,
+                     const moe_shared* shared, float* y, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int r;
+    moe::DecodePlan plan;
+    if ((r = layer_decode_checks(d, x, Wr, expert_ptrs, shared, y, idx_out, w_out, &plan))) return r;
+    if ((r = check_ws(ws, ws_bytes, moe::decode_ws_bytes(d->H, d->I, d->k, d->E)))) return r;
+    return layer_decode_launch(d, plan, x, Wr, expert_ptrs, shared, y, idx_out, w_out, ws, stream);
+}
+
+int moe_layer_decode_noalloc(const moe_desc* d, const float* x, const float* Wr, const void* const* expert_ptrs,
+                             const moe_shared* shared, float* y, int32_t* idx_out, float* w_out, void* stream) {
+    int r;
+    moe::DecodePlan plan;
+    if ((r = layer_decode_checks(d, x, Wr, expert_ptrs, shared, y, idx_out, w_out, &plan))) return r;
+    const size_t need = moe::decode_ws_bytes(d->H, d->I, d->k, d->E);
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "this layer needs %zu bytes of scratch; the static scratch holds %zu", need,
+                    kScratchBytes);
+    void* ws = nullptr;
+    if ((r = scratch_address(&ws))) return r;
+    return layer_decode_launch(d, plan, x, Wr, expert_ptrs, shared, y, idx_out, w_out, ws, stream);
 }
 
 int moe_expert_prefill(const moe_desc* d, const float* x, int32_t T, const void* const* expert_ptrs,

@@ -177,6 +177,30 @@ int moe_layer_decode(const moe_desc *d, const float *x, const float *Wr, const v
                      void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Decode without a workspace                                              */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the static scratch array behind moe_layer_decode_noalloc. Every
+ * shape moe_layer_decode supports needs at most 565,504 bytes. */
+#define MOE_NOALLOC_SCRATCH_BYTES 1048576
+
+/* moe_layer_decode for callers that cannot allocate memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation. Same arguments minus the workspace, same kernels, bit-identical
+ * results. The workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; its address on the current device is looked up
+ * on the first call there (hipGetSymbolAddress). No call allocates or frees
+ * memory. Nothing in the array carries over from one call to the next, but
+ * all calls on one GPU share it: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must not be issued; calls ordered on
+ * one stream are fine. Errors: those of moe_layer_decode (apart from the
+ * workspace ones); MOE_ERR_WORKSPACE if a layer would need more than
+ * MOE_NOALLOC_SCRATCH_BYTES; MOE_ERR_HIP if the lookup fails. */
+int moe_layer_decode_noalloc(const moe_desc *d, const float *x, const float *Wr, const void *const *expert_ptrs,
+                             const moe_shared *shared, float *y, int32_t *idx_out, float *w_out, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Prefill: T tokens grouped by expert                                     */
 /* ---------------------------------------------------------------------- */
 

@@ -108,6 +108,29 @@ def test_layer_decode_argument_errors():
     assert call(a0=m.desc(2560, 640, 512, 0, "nvfp4")) == m.MOE_ERR_ARG
 
 
+def test_layer_decode_noalloc_argument_errors():
+    """Argument errors come before the scratch lookup (no device needed), and
+    the largest supported layer fits the static scratch."""
+    d = m.desc(2560, 640, 512, 10, "nvfp4")
+    args = [d, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return _err(m.moe_layer_decode_noalloc, *a)
+
+    assert call(a1=None) == m.MOE_ERR_ARG
+    assert call(a2=FAKE + 4) == m.MOE_ERR_ARG
+    assert call(a3=None) == m.MOE_ERR_ARG
+    assert call(a4=(FAKE, None, FAKE)) == m.MOE_ERR_ARG
+    assert call(a7=FAKE + 2) == m.MOE_ERR_ARG
+    assert call(a0=m.desc(2560, 640, 2048, 10, "nvfp4")) == m.MOE_ERR_UNSUPPORTED
+    assert call(a0=m.desc(2560, 8192, 512, 10, "nvfp4")) == m.MOE_ERR_UNSUPPORTED
+    big = m.desc(4096, 4096, 1024, 32, "nvfp4")
+    assert m.moe_workspace_bytes(big, 1, m.MOE_MODE_DECODE) <= m.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_fp8_argument_errors():
     q = m.moe_act_quant_fp8
     q(FAKE, 0, 4096, 32, 0, FAKE, FAKE, 0)  # empty: nothing enqueued, MOE_OK
