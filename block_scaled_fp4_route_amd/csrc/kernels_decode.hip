@@ -7,20 +7,21 @@
 //  * down items: a block of 8 output rows of one chosen expert (or of the
 //    shared expert) against its hidden vector, per wave; the down launch
 //    then forms the weighted combine in fixed expert order in LDS.
-// Fused layer entry point, three launches:
-//  1. router rows + the shared expert's gate/up (neither needs the routing);
-//  2. top-k, recomputed at the start of every routed gate/up workgroup,
-//     + the routed gate/up tiles + the shared expert's down rows (which
-//     stream from HBM while the top-k is being computed);
-//  3. routed down items + combine (adding the shared rows of launch 2).
+// moe_expert_decode is two launches (gate/up, then down + combine);
+// moe_layer_decode puts the router GEMV in front of them (three launches),
+// and its gate/up launch selects each routed workgroup's expert from the
+// router logits itself.
 // Kernel boundaries carry the dependencies: on this chip they are cheaper
-// than in-kernel device-scope hand-offs between workgroups.
+// than in-kernel device-scope hand-offs between workgroups (an empty launch
+// in a graph costs about 1.5 us; a hand-off through device-scope atomics
+// several times that).
 // The kernels are latency-bound chains of dependent loads, so each level is
-// kept short: the expert pointer table is staged in LDS while the routing is
-// read, the gate/up launch hands the chosen blocks' addresses to the down
-// launch, x is requested before the weights (the memory counter completes
-// in issue order, so a wait for x never waits for weights), and every weight
-// load of a wave is issued before the first one is used.
+// kept short: the loads the weight addresses depend on (the routing or the
+// router logits, then the expert pointer table) are issued first, and x
+// after them (the memory counter completes in issue order, so a wait for the
+// routing never waits for x); the gate/up launch hands the chosen blocks'
+// addresses to the down launch, and every weight load of a wave is issued
+// before the first one is used.
 // Weights are read with coalesced buffer loads (64 lanes x 4 B contiguous),
 // e2m1 pairs are converted by v_cvt_scalef32_pk_f32_fp4, the group scale is
 // applied once per 8 codes in registers, and rows are reduced with DPP.
@@ -34,10 +35,11 @@ constexpr int kDownRB = 8;  // output rows per down workgroup
 constexpr int kDownNJ = 1;  // routed items per wave in the down launch (16-lane rows)
 
 // Workspace regions after the reserved bytes: h [(k+1)][I], logits [E],
-// chosen block addresses [k], shared-expert down rows [H].
+// chosen block addresses [k].
 size_t decode_ws_bytes(int H, int I, int k, int E) {
+    (void)H;
     return kCounterBytes + align256((size_t)(k + 1) * I * sizeof(float)) + align256((size_t)E * sizeof(float)) +
-           align256((size_t)k * sizeof(void*)) + align256((size_t)H * sizeof(float));
+           align256((size_t)k * sizeof(void*));
 }
 
 bool plan_decode(int fmt, int H, int I, DecodePlan* p) {
@@ -75,14 +77,12 @@ struct DecodeArgs {
     float* w_out;            // [k]
     const void** sel;        // [k] block addresses of the chosen experts (NULL: invalid index)
     float* h;                // [(k+1)][I] SwiGLU hidden vectors (slot k = shared)
-    float* ysh;              // [H] shared expert's down rows (layer entry point)
     float* y;                // [H]
     int E, k, H, I;
     int has_shared;
     int gt_r;                // gate/up tiles per routed slot
     int gt_s;                // gate/up tiles of the shared slot
     int n_items;             // down-launch items: k routed slots (+ 2 halves of the shared one)
-    int n_sd;                // shared-down workgroups in the top-k launch (layer entry point)
     uint32_t block_bytes;
 };
 
@@ -217,28 +217,6 @@ __device__ __forceinline__ void gateup_tile(const DecodeArgs& a, int slot, const
                 a.h[(size_t)slot * I + pair0 + p] = bad ? __uint_as_float(0x7FC00000u) : silu_mul(g, u);
         }
     }
-}
-
-// ----------------------------------------------------------------------------
-// Router rows: wave v of workgroup b computes logit row 4b + v, lane reads
-// float4 chunks lane + 64m (H = 256 * DV).
-template <int DV>
-__device__ __forceinline__ void router_rows(const DecodeArgs& a, int wg) {
-    const int lane = threadIdx.x & 63, e = 4 * wg + wave_id();
-    if (e >= a.E) return;
-    const f4v* xr = reinterpret_cast<const f4v*>(a.x);
-    const f4v* wr = reinterpret_cast<const f4v*>(a.Wr + (size_t)e * (256 * DV));
-    f4v p[DV], q[DV];
-#pragma unroll
-    for (int m = 0; m < DV; m++) { p[m] = wr[lane + 64 * m]; q[m] = xr[lane + 64 * m]; }
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < DV; m++) {
-        acc = fmaf(p[m].x, q[m].x, acc); acc = fmaf(p[m].y, q[m].y, acc);
-        acc = fmaf(p[m].z, q[m].z, acc); acc = fmaf(p[m].w, q[m].w, acc);
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) a.logits[e] = acc;
 }
 
 // ----------------------------------------------------------------------------
@@ -456,101 +434,102 @@ __device__ __forceinline__ void store_table(const DecodeArgs& a, const void* con
         if ((int)threadIdx.x + 256 * u < a.E) tbl[threadIdx.x + 256 * u] = t[u];
 }
 
-// moe_expert_decode, launch 1: routed gate/up tiles, then shared ones.
-// Workgroup 0 publishes the chosen blocks' addresses for the down launch.
-template <int FMT, int GD, int GP>
+// moe_layer_decode, launch 1: the router GEMV, one logit row per wave and two
+// waves per workgroup (one round of workgroups covers the chip); lane l reads
+// float4 chunks l + 64m of the row and of x (H = 256 * DV).
+template <int DV>
+__global__ __launch_bounds__(128) void k_router(DecodeArgs a) {
+    const int lane = threadIdx.x & 63, e = blockIdx.x * 2 + wave_id();
+    if (e >= a.E) return;
+    const f4v* xr = reinterpret_cast<const f4v*>(a.x);
+    const f4v* wr = reinterpret_cast<const f4v*>(a.Wr + (size_t)e * (256 * DV));
+    f4v p[DV], q[DV];
+#pragma unroll
+    for (int m = 0; m < DV; m++) { p[m] = wr[lane + 64 * m]; q[m] = xr[lane + 64 * m]; }
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < DV; m++) {
+        acc = fmaf(p[m].x, q[m].x, acc); acc = fmaf(p[m].y, q[m].y, acc);
+        acc = fmaf(p[m].z, q[m].z, acc); acc = fmaf(p[m].w, q[m].w, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) a.logits[e] = acc;
+}
+
+// Gate/up launch of both entry points: the routed gate/up tiles, then the
+// shared expert's. TNI = 0 (moe_expert_decode): the routing is given, and
+// workgroup 0 publishes the chosen blocks' addresses for the down launch.
+// TNI > 0 (moe_layer_decode): every routed workgroup selects the experts
+// from the router logits (TNI per lane of its first wave, E <= 64 TNI), up to
+// its own slot, so that early slots start streaming early; the first
+// workgroup of the last slot, which runs all k rounds, publishes the routing,
+// the weights and the chosen blocks' addresses. The loads the weight
+// addresses depend on go first (the routing or the logits, then the expert
+// pointer table, staged in LDS), x after them.
+template <int FMT, int GD, int GP, int TNI>
 __global__ __launch_bounds__(256) void k_gateup(DecodeArgs a) {
     __shared__ f4v buf[1024];  // x, H <= 4096
     __shared__ const void* tbl[kMaxE];
-    const int bid = blockIdx.x, ng_r = a.k * a.gt_r, v = wave_id();
-    XStage<512 * GD> xst;
-    xst.load(a.x);
-    if (bid < ng_r) {
-        const int slot = bid / a.gt_r;
-        const int e = a.idx[slot];
-        const int ej = a.idx[min((int)threadIdx.x, a.k - 1)];  // used by workgroup 0, lanes < k
-        const void* t[kTableRegs];
-        load_table(a, t);
-        store_table(a, t, tbl);
-        lds_barrier();
-        if (bid == 0 && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, ej);
-        gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, e), ((bid % a.gt_r) * 4 + v) * GP, buf, xst);
-    } else {
-        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (bid - ng_r) * 4 + v, buf, xst);
-    }
-}
-
-// moe_layer_decode, launch 1: router rows, then the shared expert's gate/up.
-template <int FMT, int GD>
-__global__ __launch_bounds__(256) void k_router_shared(DecodeArgs a) {
-    __shared__ f4v buf[1024];
-    const int nr = (a.E + 3) / 4;
-    if ((int)blockIdx.x < nr) {
-        router_rows<2 * GD>(a, blockIdx.x);
-    } else {
+    __shared__ int sel_e;
+    constexpr int NTB = TNI > 0 ? (64 * TNI + 255) / 256 : kTableRegs;  // table entries per thread
+    const int bid = blockIdx.x, ng_r = a.k * a.gt_r, t = threadIdx.x;
+    if (bid >= ng_r) {
         XStage<512 * GD> xst;
         xst.load(a.x);
-        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (blockIdx.x - nr) * 4 + wave_id(), buf, xst);
-    }
-}
-
-// moe_layer_decode, launch 2. Routed workgroups: every one selects the top
-// slot+1 experts from the logits (the same selection rounds in every
-// workgroup, stopped once its own slot is known, so that early slots start
-// streaming early) while x and the pointer table arrive; the first
-// workgroup of the last slot, which runs all k rounds, publishes the
-// routing and the chosen blocks' addresses; then the routed gate/up tile. The last n_sd workgroups: the shared expert's
-// down rows into ysh, half a row block per wave (the same rows and passes
-// as the down launch's shared items).
-template <int FMT, int GD, int GP, int DL, int DD>
-__global__ __launch_bounds__(256) void k_topk_gateup(DecodeArgs a) {
-    __shared__ f4v buf[1024];
-    __shared__ const void* tbl[kMaxE];
-    __shared__ int sel_e;
-    const int bid = blockIdx.x, ng_r = a.k * a.gt_r;
-    if (bid >= ng_r) {
-        constexpr int PASSES = kDownRB / (64 / DL);
-        const int half = (bid - ng_r) * 4 + wave_id(), rb = half / 2;
-        if (rb * kDownRB < a.H)
-            down_item<FMT, DL, DD, true, false>(a, a.k, nullptr, rb, (half % 2) * (PASSES / 2), PASSES / 2,
-                                                a.ysh + rb * kDownRB, nullptr);
+        gateup_tile<FMT, GD, 1, true>(a, a.k, nullptr, (bid - ng_r) * 4 + wave_id(), buf, xst);
         return;
     }
     const int slot = bid / a.gt_r;
+    float f[TNI > 0 ? TNI : 1];
+    int e = -1;    // this lane's chosen expert (for the publisher)
+    int eg = 0;    // the slot's expert (given routing)
+    if constexpr (TNI > 0) {
+        if (t < 64) {
+#pragma unroll
+            for (int i = 0; i < TNI; i++) f[i] = a.logits[min(t * TNI + i, a.E - 1)];
+        }
+    } else {
+        eg = a.idx[slot];
+        e = a.idx[min(t, a.k - 1)];  // used by workgroup 0, threads < k
+    }
+    const void* tp[NTB];
+#pragma unroll
+    for (int u = 0; u < NTB; u++) tp[u] = a.expert_ptrs[min(t + 256 * u, a.E - 1)];
     XStage<512 * GD> xst;
     xst.load(a.x);
-    const void* t[kTableRegs];
-    load_table(a, t);
-    const bool publisher = bid == (a.k - 1) * a.gt_r;
-    int e = -1;
-    float wt = 0.f;
-    if (threadIdx.x < 64) {
-        topk_select([&](int i) { return a.logits[i]; }, a.E, slot + 1, e, wt);
-        if ((int)threadIdx.x == slot) sel_e = e;
-        if (publisher && (int)threadIdx.x < a.k) {
-            a.idx_out[threadIdx.x] = e;
-            a.w_out[threadIdx.x] = wt;
+    const bool publisher = TNI > 0 ? bid == (a.k - 1) * a.gt_r : bid == 0;
+    if constexpr (TNI > 0) {
+        if (t < 64) {
+            float wt;
+            topk_select_vals<TNI>(f, a.E, publisher ? a.k : slot + 1, e, wt);
+            if (t == slot) sel_e = e;
+            if (publisher && t < a.k) {
+                a.idx_out[t] = e;
+                a.w_out[t] = wt;
+            }
         }
     }
-    store_table(a, t, tbl);
+#pragma unroll
+    for (int u = 0; u < NTB; u++)
+        if (t + 256 * u < a.E) tbl[t + 256 * u] = tp[u];
     lds_barrier();
-    if (publisher && (int)threadIdx.x < a.k) a.sel[threadIdx.x] = valid_block(a, tbl, e);
-    gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, sel_e),
+    if (publisher && t < a.k) a.sel[t] = valid_block(a, tbl, e);
+    gateup_tile<FMT, GD, GP, false>(a, slot, valid_block(a, tbl, TNI > 0 ? sel_e : eg),
                                     ((bid % a.gt_r) * 4 + wave_id()) * GP, buf, xst);
 }
 
 // down projection + combine (both entry points): one workgroup per block of
 // kDownRB output rows; wave v takes items v, v + nwaves, ... (item j < k:
-// routed slot j; items k, k+1: the two halves of the shared expert's rows,
-// present only when ysh is not used). Thread r then forms
-// y[row] = sum_j w[j] * part[j][r] (+ the shared row) in increasing j.
+// routed slot j; items k, k+1: the two halves of the shared expert's rows).
+// Thread r then forms y[row] = sum_j w[j] * part[j][r] (+ the shared row)
+// in increasing j.
 // At most 16 waves (1024 threads, 128 VGPRs) where a wave's registers fit in
 // 128 (16-lane rows of up to 640 codes); 4 waves (512 VGPRs) for the widest
 // rows (more than 3584 codes); otherwise 8 waves (512 threads, 256 VGPRs).
 constexpr int down_max_waves(int L, int D) { return (L == 16 && D <= 5) ? 16 : (D >= 8 ? 4 : 8); }
 
-// SH: the shared expert's rows are items of this launch (moe_expert_decode)
-// rather than precomputed in ysh (moe_layer_decode). PAIRS (16-lane rows,
+// SH: the layer has a shared expert, whose rows are items of this launch.
+// PAIRS (16-lane rows,
 // when the units fit the workgroup): one unit per wave, routed items two at
 // a time plus one wave per shared half, so that several small workgroups
 // share a CU and a launch covers the chip in one round. Otherwise waves loop
@@ -564,9 +543,8 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
     constexpr int PASSES = kDownRB / (64 / DL);
     const int tid = threadIdx.x, wave = wave_id(), nwaves = blockDim.x >> 6;
     const int rb = blockIdx.x, k = a.k;
-    // the combine's other inputs, requested while the weights stream
+    // the combine's weights, requested while the weights stream
     if (tid < k) wsh[tid] = a.w[tid];
-    const float ysh_row = (a.ysh != nullptr && tid < kDownRB) ? a.ysh[rb * kDownRB + tid] : 0.f;
     if constexpr (PAIRS) {
         // one unit per wave: kDownNJ routed items (items w, w + npair, ...),
         // then the two halves of the shared expert's rows; the wave's kDownNJ
@@ -604,7 +582,7 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
         const int row = rb * kDownRB + tid;
         float acc = 0.f;
         for (int j = 0; j < k; j++) acc = fmaf(wsh[j], part[j][tid], acc);
-        if (a.has_shared) acc += a.ysh ? ysh_row : part[k][tid];
+        if (a.has_shared) acc += part[k][tid];
         a.y[row] = acc;
     }
 }
@@ -1100,63 +1078,44 @@ static hipError_t launch_down(const DecodePlan& p, DecodeArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMT>
-static hipError_t launch_expert(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
-    if (use_stream(a)) return launch_stream<FMT, false>(a, s);
+// gate/up launch: TNI = 0 (routing given) or the logits per lane of the
+// in-kernel top-k (the smallest that holds E)
+template <int FMT, int TNI>
+static hipError_t launch_gateup(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
     const int n_gate = a.k * a.gt_r + (a.has_shared ? a.gt_s : 0);
-#define GU(GD, GP) case GD: hipLaunchKernelGGL((k_gateup<FMT, GD, GP>), dim3(n_gate), dim3(256), 0, s, a); break;
+#define GU(GD, GP) case GD: hipLaunchKernelGGL((k_gateup<FMT, GD, GP, TNI>), dim3(n_gate), dim3(256), 0, s, a); break;
     switch (p.gate_D) {
         GU(1, 4) GU(2, 4) GU(3, 4) GU(4, 4) GU(5, 2) GU(6, 2) GU(7, 2) GU(8, 2)
         default: return hipErrorInvalidValue;
     }
 #undef GU
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_down<FMT>(p, a, s);
-}
-
-template <int FMT, int GD, int GP>
-static hipError_t launch_topk_gateup(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
-    dim3 grid(a.k * a.gt_r + a.n_sd), block(256);
-#define TG(DL, DD) case DD: hipLaunchKernelGGL((k_topk_gateup<FMT, GD, GP, DL, DD>), grid, block, 0, s, a); break;
-    if (p.down_L == 16) {
-        switch (p.down_D) {
-            TG(16, 1) TG(16, 2) TG(16, 3) TG(16, 4) TG(16, 5) TG(16, 6) TG(16, 7) TG(16, 8)
-            default: return hipErrorInvalidValue;
-        }
-    } else {
-        switch (p.down_D) {
-            TG(64, 1) TG(64, 2) TG(64, 3) TG(64, 4) TG(64, 5) TG(64, 6) TG(64, 7) TG(64, 8)
-            default: return hipErrorInvalidValue;
-        }
-    }
-#undef TG
     return hipGetLastError();
 }
 
 template <int FMT>
+static hipError_t launch_expert(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
+    if (use_stream(a)) return launch_stream<FMT, false>(a, s);
+    hipError_t e = launch_gateup<FMT, 0>(p, a, s);
+    if (e != hipSuccess) return e;
+    return launch_down<FMT>(p, a, s);
+}
+
+template <int FMT>
 static hipError_t launch_layer(const DecodePlan& p, DecodeArgs& a, hipStream_t s) {
-    const int n1 = (a.E + 3) / 4 + (a.has_shared ? a.gt_s : 0);
-#define RS(GD) case GD: hipLaunchKernelGGL((k_router_shared<FMT, GD>), dim3(n1), dim3(256), 0, s, a); break;
+#define RT(GD) case GD: hipLaunchKernelGGL((k_router<2 * GD>), dim3((a.E + 1) / 2), dim3(128), 0, s, a); break;
     switch (p.gate_D) {
-        RS(1) RS(2) RS(3) RS(4) RS(5) RS(6) RS(7) RS(8)
+        RT(1) RT(2) RT(3) RT(4) RT(5) RT(6) RT(7) RT(8)
         default: return hipErrorInvalidValue;
     }
-#undef RS
+#undef RT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (use_stream(a)) return launch_stream<FMT, true>(a, s);
-    switch (p.gate_D) {
-        case 1: e = launch_topk_gateup<FMT, 1, 4>(p, a, s); break;
-        case 2: e = launch_topk_gateup<FMT, 2, 4>(p, a, s); break;
-        case 3: e = launch_topk_gateup<FMT, 3, 4>(p, a, s); break;
-        case 4: e = launch_topk_gateup<FMT, 4, 4>(p, a, s); break;
-        case 5: e = launch_topk_gateup<FMT, 5, 2>(p, a, s); break;
-        case 6: e = launch_topk_gateup<FMT, 6, 2>(p, a, s); break;
-        case 7: e = launch_topk_gateup<FMT, 7, 2>(p, a, s); break;
-        case 8: e = launch_topk_gateup<FMT, 8, 2>(p, a, s); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (a.E <= 64) e = launch_gateup<FMT, 1>(p, a, s);
+    else if (a.E <= 128) e = launch_gateup<FMT, 2>(p, a, s);
+    else if (a.E <= 256) e = launch_gateup<FMT, 4>(p, a, s);
+    else if (a.E <= 512) e = launch_gateup<FMT, 8>(p, a, s);
+    else e = launch_gateup<FMT, 16>(p, a, s);
     if (e != hipSuccess) return e;
     return launch_down<FMT>(p, a, s);
 }
@@ -1173,7 +1132,6 @@ static DecodeArgs make_args(const DecodePlan& p, int fmt, int E, int H, int I, i
     a.h = reinterpret_cast<float*>(base + kCounterBytes);
     a.logits = reinterpret_cast<float*>(base + kCounterBytes + h_bytes);
     a.sel = reinterpret_cast<const void**>(base + kCounterBytes + h_bytes + l_bytes);
-    a.ysh = nullptr;
     a.y = y;
     a.E = E; a.k = k; a.H = H; a.I = I;
     a.has_shared = sh_gate ? 1 : 0;
@@ -1204,13 +1162,6 @@ hipError_t launch_layer_decode(int fmt, const DecodePlan& p, int E, int H, int I
     a.idx_out = idx_out;
     a.w_out = w_out;
     a.w = w_out;  // the down launch reads the published weights
-    if (a.has_shared) {
-        // the shared expert's down rows move to the top-k launch
-        const size_t sel_bytes = align256((size_t)k * sizeof(void*));
-        a.ysh = reinterpret_cast<float*>(reinterpret_cast<char*>(a.sel) + sel_bytes);
-        a.n_items = k;
-        a.n_sd = (2 * (H / kDownRB) + 3) / 4;
-    }
     return fmt == kFmtNvfp4 ? launch_layer<kFmtNvfp4>(p, a, s) : launch_layer<kFmtMxfp4>(p, a, s);
 }
 

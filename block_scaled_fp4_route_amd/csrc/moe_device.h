@@ -174,24 +174,21 @@ constexpr int kTopkMaxE = 1024;
 // Top-k of E <= 64 * NI logits by one full wave: afterwards lane j < kk
 // holds the j-th chosen expert (larger logit first, lower expert index first
 // among equal logits) in my_e and its weight, the softmax renormalised over
-// the first kk chosen, in my_w. LOAD(e) reads logit e (0 <= e < E); kk <= E.
+// the first kk chosen, in my_w. f[i] is logit lane * NI + i of this lane
+// (any value past E - 1); kk <= E.
 // The logits are compared as order-preserving integer keys (-0 folded onto
 // +0; a NaN ranks above +inf, so every chosen index is in [0, E)).
 // Lane l holds experts l*NI .. l*NI + NI - 1 and first sorts them (key
 // descending, then index ascending; Batcher's odd-even merge network over
 // registers). A round then only compares the lanes' heads: the largest head
 // wins, and among equal heads the lowest lane, which holds the lowest expert
-// indices; the winning lane shifts its sorted list by one. All loads are
-// issued before the first use (no load under a branch).
-template <int NI, class LOAD>
-__device__ __forceinline__ void topk_select_n(LOAD load, int E, int kk, int& my_e, float& my_w) {
+// indices; the winning lane shifts its sorted list by one.
+template <int NI>
+__device__ __forceinline__ void topk_select_vals(const float (&f)[NI], int E, int kk, int& my_e, float& my_w) {
     const int lane = threadIdx.x & 63;
     uint32_t v[NI];
     int ix[NI];
     {
-        float f[NI];
-#pragma unroll
-        for (int i = 0; i < NI; i++) f[i] = load(min(lane * NI + i, E - 1));
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             v[i] = lane * NI + i < E ? f32_key(f[i] + 0.0f) : 0u;  // + 0 folds -0 onto +0; 0 = padding
@@ -246,6 +243,17 @@ __device__ __forceinline__ void topk_select_n(LOAD load, int E, int kk, int& my_
     const float ex = lane < kk ? expf(my_l - lmax) : 0.f;
     const float z = wave_sum(ex);
     my_w = ex / z;
+}
+
+// As topk_select_vals, the logits read by LOAD(e) (0 <= e < E); all loads
+// are issued before the first use.
+template <int NI, class LOAD>
+__device__ __forceinline__ void topk_select_n(LOAD load, int E, int kk, int& my_e, float& my_w) {
+    const int lane = threadIdx.x & 63;
+    float f[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) f[i] = load(min(lane * NI + i, E - 1));
+    topk_select_vals<NI>(f, E, kk, my_e, my_w);
 }
 
 // topk_select_n with the smallest register count that holds E logits.

@@ -181,7 +181,7 @@ int moe_layer_decode(const moe_desc *d, const float *x, const float *Wr, const v
 /* ---------------------------------------------------------------------- */
 
 /* Bytes of the static scratch array behind moe_layer_decode_noalloc. Every
- * shape moe_layer_decode supports needs at most 565,504 bytes. */
+ * shape moe_layer_decode supports needs at most 549,120 bytes. */
 #define MOE_NOALLOC_SCRATCH_BYTES 1048576
 
 /* moe_layer_decode for callers that cannot allocate memory: code being
