@@ -472,6 +472,11 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 // row r at slot r*SPR + (p ^ (r & 7)), which keeps the fragment reads of 8
 // consecutive rows on distinct bank groups. Rows past `rows` take the
 // out-of-range offset (zeros, no memory traffic; their sums are never stored).
+// SL: the block scales of the workgroup's weight rows were staged in LDS
+// before the loop (slds: row n - srow0 at (n - srow0) * KTOT/16, the rows'
+// scale bytes as stored), so the loop loads only codes from memory. A scale
+// load from memory takes a whole cache line for 2-4 bytes of each row; staged,
+// the rows' scales arrive as contiguous lines once.
 
 // 16-byte buffer load straight into LDS: lane l writes lds + 16*l (lds is
 // wave-uniform).
@@ -483,17 +488,17 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off)
 // code that uses a or b after it cannot be scheduled before it.
 __device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
-template <int BK, int RB, class AROW>
+template <int BK, int RB, bool SL, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
                                          uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
-                                         __bf16* lds) {
+                                         __bf16* lds, const uint8_t* slds, int srow0) {
     constexpr int SPR = BK / 8;       // 16-byte pieces per A row
     constexpr int NAI = SPR / 4;      // A loads per wave per chunk (64 rows x SPR pieces over 256 lanes)
     constexpr int QK = BK / 4;        // K per lane group
     constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
     constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
-    constexpr int NBL = 4 * (NB + 1); // weight loads per lane per chunk (codes + scales)
+    constexpr int NBL = SL ? 4 * NB : 4 * (NB + 1);  // weight loads per lane per chunk (codes [+ scales])
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, m16 = lane & 15;
     const rsrc_t ra = make_rsrc(A, a_bytes);
@@ -531,9 +536,11 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, on ? boff[cb] + ch * (BK / 2) + 16 * i : kOOB, 0, 0);
                 bw[cb][i] = uint4{v[0], v[1], v[2], v[3]};
             }
-            const uint32_t so = on ? soff[cb] + ch * (BK / 16) : kOOB;
-            bs[cb] = NB == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b32(rb, so, 0, 0);
+            if constexpr (!SL) {
+                const uint32_t so = on ? soff[cb] + ch * (BK / 16) : kOOB;
+                bs[cb] = NB == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0)
+                                 : __builtin_amdgcn_raw_buffer_load_b32(rb, so, 0, 0);
+            }
         }
     };
     uint4 b0[4][NB], b1[4][NB];
@@ -553,7 +560,12 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
         for (int cb = 0; cb < 4; cb++) {
 #pragma unroll
             for (int i = 0; i < NB; i++) bc[cb][i] = bw[cb][i];
-            sc[cb] = bs[cb];
+            if constexpr (SL) {
+                const uint8_t* sp = slds + (brow[cb] - srow0) * (KTOT / 16) + ch * (BK / 16) + (QK / 16) * g;
+                sc[cb] = NB == 1 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : *reinterpret_cast<const uint32_t*>(sp);
+            } else {
+                sc[cb] = bs[cb];
+            }
         }
         issue_a(ch + 1, (ch + 1) & 1);
         load_b(ch + 2, bw, bs);
@@ -621,11 +633,11 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the K loop is specialised on the tile's row blocks (wave-uniform)
     if (rows <= 16)
-        nv_kloop<kBKGate, 1>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
+        nv_kloop<kBKGate, 1, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds, nullptr, 0);
     else if (rows <= 32)
-        nv_kloop<kBKGate, 2>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
+        nv_kloop<kBKGate, 2, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds, nullptr, 0);
     else
-        nv_kloop<kBKGate, 4>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds);
+        nv_kloop<kBKGate, 4, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds, nullptr, 0);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
     const int g = lane >> 4;
@@ -650,8 +662,14 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
 // 4b. NVFP4 down: Y[p][n] = sum_i h~[p][i] * Wd[n][i]. Workgroup = (M-tile of
 // 64 grouped rows, 256 columns of H); wave w owns columns n0 + 64w .. +64 as
 // 4 column blocks of 16. A rows are contiguous grouped rows of h~.
+// SL (I <= kDownSclMaxI): the scales of the 256 weight rows (I/16 bytes each,
+// contiguous in the block) are staged in LDS first; the K loop then reads
+// only codes from memory.
+constexpr int kDownSclMaxI = 1024;
+template <bool SL>
 __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
     __shared__ __bf16 lds[2 * 64 * kBKDown];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[SL ? 256 * kDownSclMaxI / 16 : 16];
     int tile, nt;
     if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
@@ -667,17 +685,27 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
     const int brow[4] = {n0 + m16, n0 + 16 + m16, n0 + 32 + m16, n0 + 48 + m16};
     const __bf16* Hq = reinterpret_cast<const __bf16*>(a.a_src);
     auto a_row = [&](int r) { return (base + r) * I; };  // 0 <= r < rows
+    if constexpr (SL) {
+        // 1 KB loads of the rows' scales; they are older than the K loop's
+        // first loads, so its first wait covers them
+        const uint32_t SB = (uint32_t)I / 16, tot = 256 * SB, s0 = scl_off + (uint32_t)(nt * 256) * SB;
+        const rsrc_t rw = make_rsrc(blk, a.block_bytes);
+        for (uint32_t ii = wave; ii * 1024 < tot; ii += 4) {
+            const uint32_t b = ii * 1024 + 16 * lane;
+            load_lds16(rw, sl + ii * 1024, b < tot ? s0 + b : kOOB);
+        }
+    }
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (rows <= 16)
-        nv_kloop<kBKDown, 1>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
+        nv_kloop<kBKDown, 1, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds, sl, nt * 256);
     else if (rows <= 32)
-        nv_kloop<kBKDown, 2>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
+        nv_kloop<kBKDown, 2, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds, sl, nt * 256);
     else
-        nv_kloop<kBKDown, 4>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds);
+        nv_kloop<kBKDown, 4, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds, sl, nt * 256);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
@@ -1060,7 +1088,10 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         GemmArgs gd = ga;
         gd.a_src = L.hq; gd.out = L.Y; gd.h_pre = nullptr; gd.h_q = nullptr; gd.NT = H / 256;
         gd.a_bytes = (uint32_t)((size_t)n * I * 2);
-        hipLaunchKernelGGL(k_down_nv, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+        if (I <= kDownSclMaxI)
+            hipLaunchKernelGGL(k_down_nv<true>, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+        else
+            hipLaunchKernelGGL(k_down_nv<false>, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     } else {
         uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);

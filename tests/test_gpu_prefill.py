@@ -275,6 +275,14 @@ def test_prefill_nvfp4_qwen_shape_small_E(m, orc):
     full_check(m, orc, wl, 40)
 
 
+@pytest.mark.parametrize("H,I,E,k,T", [(768, 1024, 6, 3, 70), (512, 1152, 5, 2, 40)])
+def test_prefill_nvfp4_down_scale_staging(m, orc, H, I, E, k, T):
+    """The NVFP4 down GEMM stages its weight rows' scales in LDS up to
+    I = 1024 (256 rows x 64 scale bytes) and loads them per chunk above it:
+    both forms, with tiles of more than one row block."""
+    full_check(m, orc, wl_small("nvfp4", H, I, E, k, T), T)
+
+
 def test_prefill_mxfp4_deepseek_shape_small_E(m, orc):
     wl = wl_small("mxfp4", 4096, 2880, 12, 6, 20, s=0.0)
     full_check(m, orc, wl, 20)
