@@ -26,7 +26,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBM_NV = 64;  // NVFP4 M-tile (rows of one expert)
+constexpr int kBM_NV = 64;    // NVFP4 M-tile (rows of one expert)
+constexpr int kBM_NV2 = 128;  // NVFP4 M-tile of the experts with at least this many rows
 constexpr int kBM_MX = 32;  // MXFP4 M-tile
 constexpr int kGroupThreads = 1024;
 
@@ -210,7 +211,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
 
 // ---------------------------------------------------------------------------
 // 2. tile list: experts ordered by row count (descending; ties by index),
-// each split into M-tiles of BM rows.
+// each split into M-tiles of BM rows, or of BM2 rows if it has at least BM2
+// (BM2 = 0: one height).
 //
 // With rec != nullptr it also writes one record per slot of the max_tiles
 // slots: the expert block, the first grouped row and the row count of the
@@ -223,7 +225,7 @@ struct TileRec {
 };
 static_assert(sizeof(TileRec) == 16, "tile record is 16 bytes");
 
-__global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restrict__ count, int E, int BM,
+__global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restrict__ count, int E, int BM, int BM2,
                                                              int* __restrict__ tile_e, int* __restrict__ tile_m,
                                                              int* __restrict__ ntiles, TileRec* __restrict__ rec,
                                                              int max_slots, const int* __restrict__ off,
@@ -264,9 +266,10 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
         atomicAdd(&rank[e], r);
     }
     __syncthreads();
+    auto height = [&](int c) { return BM2 > 0 && c >= BM2 ? BM2 : BM; };
     for (int e = tid; e < E; e += kGroupThreads) {
         ex_sorted[rank[e]] = e;
-        nt_sorted[rank[e]] = (cnt[e] + BM - 1) / BM;
+        nt_sorted[rank[e]] = (cnt[e] + height(cnt[e]) - 1) / height(cnt[e]);
     }
     __syncthreads();
     // inclusive scan of nt_sorted (Hillis-Steele over kGroupThreads >= E entries)
@@ -298,14 +301,14 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
             const int mid = (lo + hi + 1) >> 1;
             if (start[mid] <= sl) lo = mid; else hi = mid - 1;
         }
-        const int e = ex_sorted[lo], m = sl - start[lo];
+        const int e = ex_sorted[lo], bm = height(cnt[e]), m = sl - start[lo];
         tile_e[sl] = e;
-        tile_m[sl] = m * BM;
+        tile_m[sl] = m * bm;
         if (rec) {
             TileRec t;
             t.blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
-            t.base = off[e] + m * BM;
-            t.rows = min(BM, cnt[e] - m * BM);
+            t.base = off[e] + m * bm;
+            t.rows = min(bm, cnt[e] - m * bm);
             rec[sl] = t;
         }
     }
@@ -385,10 +388,14 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
 // ---------------------------------------------------------------------------
 // 4a. NVFP4 gate/up: ragged grouped GEMM with bf16 MFMA.
 //
-// Workgroup = (M-tile of 64 rows of one expert, 128 output columns of I).
+// Workgroup = (M-tile of one expert, 128 output columns of I). M-tiles are
+// 128 rows for the experts that have at least 128 rows and 64 rows for the
+// rest: a decoded weight fragment then serves up to 8 row blocks, which halves
+// the decode work and the weight loads per MFMA of the heavy experts.
 // Wave w owns output columns c0 = n0 + 32w .. +32 of BOTH gate and up, so its
 // B operand is 4 column blocks of 16 (gate c0, gate c0+16, up c0, up c0+16)
-// and SiLU*mul happens in registers. K runs over H in chunks of 256; within a
+// and SiLU*mul happens in registers. K runs over H in chunks of 256 (128 for
+// the 128-row tiles, whose A tile then takes the same LDS); within a
 // chunk each lane group owns a contiguous quarter of K (see nv_kloop), with
 // the A operand read from LDS under the same K mapping (the dot product is
 // order-independent). The codes are decoded to bf16 exactly (e2m1 x E4M3 has
@@ -451,8 +458,9 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
     return o;
 }
 
-// Shared K loop of the two NVFP4 GEMMs: acc[rb][cb] += A[64 rows] x B[4
-// column blocks]^T over K (= KTOT) in chunks of BK (128 or 256). A is a
+// Shared K loop of the two NVFP4 GEMMs: acc[rb][cb] += A[16 RB rows] x B[4
+// column blocks]^T over K (= KTOT) in chunks of BK (128 or 256), the A tile
+// staged in LDS as MR rows (64 or 128; RB <= MR/16) per chunk. A is a
 // buffer of a_bytes bytes; a_row(r) gives the element offset of A row r
 // (0 <= r < rows). blk is the expert block (block_bytes), codes_off and
 // scl_off the byte offsets of the weight matrix's code and scale regions
@@ -488,13 +496,13 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off)
 // code that uses a or b after it cannot be scheduled before it.
 __device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
-template <int BK, int RB, bool SL, class AROW>
-__device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __restrict__ A, uint32_t a_bytes,
+template <int BK, int RB, int MR, bool SL, class AROW>
+__device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
                                          uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
                                          __bf16* lds, const uint8_t* slds, int srow0) {
     constexpr int SPR = BK / 8;       // 16-byte pieces per A row
-    constexpr int NAI = SPR / 4;      // A loads per wave per chunk (64 rows x SPR pieces over 256 lanes)
+    constexpr int NAI = MR * SPR / 256;  // A loads per wave per chunk (MR rows x SPR pieces over 256 lanes)
     constexpr int QK = BK / 4;        // K per lane group
     constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
     constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
@@ -524,7 +532,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
 #pragma unroll
         for (int i = 0; i < NAI; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (__attribute__((address_space(3))) void*)(lds + (size_t)buf * 64 * BK + (size_t)(wave * NAI + i) * 64 * 8),
+                ra, (__attribute__((address_space(3))) void*)(lds + (size_t)buf * MR * BK + (size_t)(wave * NAI + i) * 64 * 8),
                 16, on && aon[i] ? aoff[i] + 2u * ch * BK : kOOB, 0, 0, 0);
     };
     auto load_b = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4]) {
@@ -543,14 +551,17 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
             }
         }
     };
+    // weight register sets: two (chunks ch+1 and ch+2 in flight), or one for
+    // 8 row blocks, whose accumulators leave no room for a second set
+    constexpr int NSET = RB >= 8 ? 1 : 2;
     uint4 b0[4][NB], b1[4][NB];
     uint32_t s0[4], s1[4];
     issue_a(0, 0);
     load_b(0, b0, s0);
-    load_b(1, b1, s1);
-    vm_wait_barrier<NBL>();  // A(0) (and B(0)) landed
+    if constexpr (NSET > 1) load_b(1, b1, s1);
+    vm_wait_barrier<NBL>();  // A(0) landed
     // one chunk: take its weights out of set (bw, bs), refill the set with
-    // chunk ch+2, load A(ch+1) into the other LDS buffer, compute, then wait
+    // chunk ch+NSET, load A(ch+1) into the other LDS buffer, compute, then wait
     // for A(ch+1): the barrier also ends every wave's reads of this chunk's
     // buffer, which A(ch+2) overwrites
     auto step = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4]) {
@@ -568,12 +579,12 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
             }
         }
         issue_a(ch + 1, (ch + 1) & 1);
-        load_b(ch + 2, bw, bs);
+        load_b(ch + NSET, bw, bs);
         if (ch < nchunks) {
-            const __bf16* At = lds + (size_t)(ch & 1) * 64 * BK;
+            const __bf16* At = lds + (size_t)(ch & 1) * MR * BK;
 #pragma unroll
             for (int s = 0; s < NS; s++) {
-                // the A fragments of all row blocks first (the 64-row tile is
+                // the A fragments of all row blocks first (the MR-row tile is
                 // always allocated), so their LDS latency hides behind the decode
                 const int p = (QK / 8) * g + s;  // 16-byte piece of the fragment
                 bf16x8 af[RB];
@@ -598,22 +609,23 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[4][4], const __bf16* __res
         }
         vm_wait_barrier<NBL>();
     };
-    for (int ch = 0; ch < nchunks; ch += 2) {
-        step(ch, b0, s0);
-        step(ch + 1, b1, s1);
+    if constexpr (NSET > 1) {
+        for (int ch = 0; ch < nchunks; ch += 2) {
+            step(ch, b0, s0);
+            step(ch + 1, b1, s1);
+        }
+    } else {
+        for (int ch = 0; ch < nchunks; ch++) step(ch, b0, s0);
     }
 }
 
 constexpr int kBKGate = 256;  // K chunk of the gate/up GEMM (K = H)
 constexpr int kBKDown = 128;  // K chunk of the down GEMM (K = I)
 
-__global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * kBKGate];
-    int tile, nt;
-    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
-    const int e = a.tile_e[tile], m0 = a.tile_m[tile];
-    const int rows = min(kBM_NV, a.count[e] - m0);
-    const int base = a.off[e] + m0;
+// One gate/up tile: RB row blocks of the tile's rows, K chunks of BK, the A
+// tile staged as MR rows.
+template <int RB, int BK, int MR>
+__device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, int e, int base, int rows, int nt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int c0 = nt * 128 + 32 * wave;
@@ -626,23 +638,18 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
     const int* perm = a.perm;
     const int k = a.k;
     auto a_row = [&](int r) { return (perm[base + r] / k) * H; };  // 0 <= r < rows
-    f32x4 acc[4][4];
+    f32x4 acc[RB][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the K loop is specialised on the tile's row blocks (wave-uniform)
-    if (rows <= 16)
-        nv_kloop<kBKGate, 1, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds, nullptr, 0);
-    else if (rows <= 32)
-        nv_kloop<kBKGate, 2, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds, nullptr, 0);
-    else
-        nv_kloop<kBKGate, 4, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds, nullptr, 0);
+    nv_kloop<BK, RB, MR, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds,
+                                nullptr, 0);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
+    for (int rb = 0; rb < RB; rb++)
 #pragma unroll
         for (int cbg = 0; cbg < 2; cbg++)
 #pragma unroll
@@ -659,22 +666,44 @@ __global__ __launch_bounds__(256) void k_gateup_nv(GemmArgs a) {
             }
 }
 
+// Rows of tile (e, m0): tiles are kBM_NV2 rows high for experts with at least
+// kBM_NV2 rows, kBM_NV otherwise (the tile list's rule).
+__device__ __forceinline__ int nv_tile_rows(const GemmArgs& a, int e, int m0) {
+    const int c = a.count[e];
+    return min(c >= kBM_NV2 ? kBM_NV2 : kBM_NV, c - m0);
+}
+
+__global__ __launch_bounds__(256, 2) void k_gateup_nv(GemmArgs a) {
+    __shared__ __bf16 lds[2 * 64 * kBKGate];  // = 2 * kBM_NV2 * 128
+    static_assert(2 * 64 * kBKGate == 2 * kBM_NV2 * 128, "one LDS size for both tile heights");
+    int tile, nt;
+    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
+    const int e = a.tile_e[tile], m0 = a.tile_m[tile];
+    const int rows = nv_tile_rows(a, e, m0);
+    const int base = a.off[e] + m0;
+    // the K loop is specialised on the tile's row blocks (wave-uniform); a
+    // 128-row tile takes 128-wide K chunks so that its A tile fits the same LDS
+    if (rows <= 16)
+        gateup_nv_tile<1, kBKGate, 64>(a, lds, e, base, rows, nt);
+    else if (rows <= 32)
+        gateup_nv_tile<2, kBKGate, 64>(a, lds, e, base, rows, nt);
+    else if (rows <= 64)
+        gateup_nv_tile<4, kBKGate, 64>(a, lds, e, base, rows, nt);
+    else
+        gateup_nv_tile<8, 128, kBM_NV2>(a, lds, e, base, rows, nt);
+}
+
 // 4b. NVFP4 down: Y[p][n] = sum_i h~[p][i] * Wd[n][i]. Workgroup = (M-tile of
-// 64 grouped rows, 256 columns of H); wave w owns columns n0 + 64w .. +64 as
+// 64 or 128 grouped rows, 256 columns of H); wave w owns columns n0 + 64w .. +64 as
 // 4 column blocks of 16. A rows are contiguous grouped rows of h~.
 // SL (I <= kDownSclMaxI): the scales of the 256 weight rows (I/16 bytes each,
 // contiguous in the block) are staged in LDS first; the K loop then reads
 // only codes from memory.
 constexpr int kDownSclMaxI = 1024;
-template <bool SL>
-__global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * kBKDown];
-    __shared__ __attribute__((aligned(16))) uint8_t sl[SL ? 256 * kDownSclMaxI / 16 : 16];
-    int tile, nt;
-    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
-    const int e = a.tile_e[tile], m0 = a.tile_m[tile];
-    const int rows = min(kBM_NV, a.count[e] - m0);
-    const int base = a.off[e] + m0;
+
+template <int RB, int MR, bool SL>
+__device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, const uint8_t* sl, int e, int base,
+                                             int rows, int nt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int n0 = nt * 256 + 64 * wave;
@@ -685,31 +714,17 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
     const int brow[4] = {n0 + m16, n0 + 16 + m16, n0 + 32 + m16, n0 + 48 + m16};
     const __bf16* Hq = reinterpret_cast<const __bf16*>(a.a_src);
     auto a_row = [&](int r) { return (base + r) * I; };  // 0 <= r < rows
-    if constexpr (SL) {
-        // 1 KB loads of the rows' scales; they are older than the K loop's
-        // first loads, so its first wait covers them
-        const uint32_t SB = (uint32_t)I / 16, tot = 256 * SB, s0 = scl_off + (uint32_t)(nt * 256) * SB;
-        const rsrc_t rw = make_rsrc(blk, a.block_bytes);
-        for (uint32_t ii = wave; ii * 1024 < tot; ii += 4) {
-            const uint32_t b = ii * 1024 + 16 * lane;
-            load_lds16(rw, sl + ii * 1024, b < tot ? s0 + b : kOOB);
-        }
-    }
-    f32x4 acc[4][4];
+    f32x4 acc[RB][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (rows <= 16)
-        nv_kloop<kBKDown, 1, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds, sl, nt * 256);
-    else if (rows <= 32)
-        nv_kloop<kBKDown, 2, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds, sl, nt * 256);
-    else
-        nv_kloop<kBKDown, 4, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds, sl, nt * 256);
+    nv_kloop<kBKDown, RB, MR, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds,
+                                  sl, nt * 256);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
+    for (int rb = 0; rb < RB; rb++)
 #pragma unroll
         for (int cb = 0; cb < 4; cb++)
 #pragma unroll
@@ -717,6 +732,37 @@ __global__ __launch_bounds__(256) void k_down_nv(GemmArgs a) {
                 const int r = 16 * rb + 4 * g + i;
                 if (r < rows) Y[(size_t)(base + r) * H + n0 + 16 * cb + m16] = acc[rb][cb][i];
             }
+}
+
+template <bool SL>
+__global__ __launch_bounds__(256, 2) void k_down_nv(GemmArgs a) {
+    __shared__ __bf16 lds[2 * kBM_NV2 * kBKDown];
+    __shared__ __attribute__((aligned(16))) uint8_t sl[SL ? 256 * kDownSclMaxI / 16 : 16];
+    int tile, nt;
+    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
+    const int e = a.tile_e[tile], m0 = a.tile_m[tile];
+    const int rows = nv_tile_rows(a, e, m0);
+    const int base = a.off[e] + m0;
+    if constexpr (SL) {
+        // 1 KB loads of the rows' scales; they are older than the K loop's
+        // first loads, so its first wait covers them
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const uint32_t SB = (uint32_t)a.I / 16, tot = 256 * SB;
+        const uint32_t s0 = (uint32_t)3 * a.I * a.H / 2 + (uint32_t)2 * a.I * a.H / 16 + (uint32_t)(nt * 256) * SB;
+        const rsrc_t rw = make_rsrc(a.expert_ptrs[e], a.block_bytes);
+        for (uint32_t ii = wave; ii * 1024 < tot; ii += 4) {
+            const uint32_t b = ii * 1024 + 16 * lane;
+            load_lds16(rw, sl + ii * 1024, b < tot ? s0 + b : kOOB);
+        }
+    }
+    if (rows <= 16)
+        down_nv_tile<1, 64, SL>(a, lds, sl, e, base, rows, nt);
+    else if (rows <= 32)
+        down_nv_tile<2, 64, SL>(a, lds, sl, e, base, rows, nt);
+    else if (rows <= 64)
+        down_nv_tile<4, 64, SL>(a, lds, sl, e, base, rows, nt);
+    else
+        down_nv_tile<8, kBM_NV2, SL>(a, lds, sl, e, base, rows, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1065,7 +1111,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     hipLaunchKernelGGL(k_group, dim3((E + kGroupExperts - 1) / kGroupExperts), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
     LAUNCH_CHECK();
     TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
-    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, L.tile_e, L.tile_m, L.ntiles,
+    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, fmt == kFmtNvfp4 ? kBM_NV2 : 0, L.tile_e, L.tile_m, L.ntiles,
                        rec, mt, off, expert_ptrs);
     LAUNCH_CHECK();
 
