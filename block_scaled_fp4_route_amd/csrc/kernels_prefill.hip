@@ -27,7 +27,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBM_NV = 64;    // NVFP4 M-tile (rows of one expert)
-constexpr int kBM_NV2 = 128;  // NVFP4 M-tile of the experts with at least this many rows
+constexpr int kBM_NV2 = 128;  // NVFP4 M-tile of the heavy experts
+constexpr int kNV2Min = 65;   // rows from which an expert is heavy (more than one 64-row tile)
 constexpr int kBM_MX = 32;  // MXFP4 M-tile
 constexpr int kGroupThreads = 1024;
 
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
 
 // ---------------------------------------------------------------------------
 // 2. tile list: experts ordered by row count (descending; ties by index),
-// each split into M-tiles of BM rows, or of BM2 rows if it has at least BM2
-// (BM2 = 0: one height).
+// each split into M-tiles of BM rows, or of BM2 rows if it has at least
+// BM2min (BM2 = 0: one height).
 //
 // With rec != nullptr it also writes one record per slot of the max_tiles
 // slots: the expert block, the first grouped row and the row count of the
@@ -225,7 +226,7 @@ struct TileRec {
 };
 static_assert(sizeof(TileRec) == 16, "tile record is 16 bytes");
 
-__global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restrict__ count, int E, int BM, int BM2,
+__global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restrict__ count, int E, int BM, int BM2, int BM2min,
                                                              int* __restrict__ tile_e, int* __restrict__ tile_m,
                                                              int* __restrict__ ntiles, TileRec* __restrict__ rec,
                                                              int max_slots, const int* __restrict__ off,
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
         atomicAdd(&rank[e], r);
     }
     __syncthreads();
-    auto height = [&](int c) { return BM2 > 0 && c >= BM2 ? BM2 : BM; };
+    auto height = [&](int c) { return BM2 > 0 && c >= BM2min ? BM2 : BM; };
     for (int e = tid; e < E; e += kGroupThreads) {
         ex_sorted[rank[e]] = e;
         nt_sorted[rank[e]] = (cnt[e] + height(cnt[e]) - 1) / height(cnt[e]);
@@ -389,9 +390,10 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
 // 4a. NVFP4 gate/up: ragged grouped GEMM with bf16 MFMA.
 //
 // Workgroup = (M-tile of one expert, 128 output columns of I). M-tiles are
-// 128 rows for the experts that have at least 128 rows and 64 rows for the
+// 128 rows for the experts that have more than 64 rows and 64 rows for the
 // rest: a decoded weight fragment then serves up to 8 row blocks, which halves
-// the decode work and the weight loads per MFMA of the heavy experts.
+// the decode work and the weight loads per MFMA of the heavy experts (an
+// expert of 65-128 rows decodes its weights once instead of twice).
 // Wave w owns output columns c0 = n0 + 32w .. +32 of BOTH gate and up, so its
 // B operand is 4 column blocks of 16 (gate c0, gate c0+16, up c0, up c0+16)
 // and SiLU*mul happens in registers. K runs over H in chunks of 256 (128 for
@@ -667,10 +669,10 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
 }
 
 // Rows of tile (e, m0): tiles are kBM_NV2 rows high for experts with at least
-// kBM_NV2 rows, kBM_NV otherwise (the tile list's rule).
+// kNV2Min rows, kBM_NV otherwise (the tile list's rule).
 __device__ __forceinline__ int nv_tile_rows(const GemmArgs& a, int e, int m0) {
     const int c = a.count[e];
-    return min(c >= kBM_NV2 ? kBM_NV2 : kBM_NV, c - m0);
+    return min(c >= kNV2Min ? kBM_NV2 : kBM_NV, c - m0);
 }
 
 __global__ __launch_bounds__(256, 2) void k_gateup_nv(GemmArgs a) {
@@ -1111,7 +1113,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     hipLaunchKernelGGL(k_group, dim3((E + kGroupExperts - 1) / kGroupExperts), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
     LAUNCH_CHECK();
     TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
-    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, fmt == kFmtNvfp4 ? kBM_NV2 : 0, L.tile_e, L.tile_m, L.ntiles,
+    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, fmt == kFmtNvfp4 ? kBM_NV2 : 0, kNV2Min, L.tile_e, L.tile_m, L.ntiles,
                        rec, mt, off, expert_ptrs);
     LAUNCH_CHECK();
 
