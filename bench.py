@@ -32,15 +32,64 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefill)"
 
 # HBM bytes per call of the roofline's kernels from rocprofv3 --pmc
-# (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain 1 GiB copy gives),
-# per workload; absent until counters were taken on the current kernels.
-# qwen_decode: k_gateup<1,5,2> + k_down_combine<1,16,5,true,true>.
+# (FETCH_SIZE x 2 + WRITE_SIZE x 1 KiB, the factors a plain 1 GiB copy gives;
+# profiles/*_hbm_traffic.md), per workload, with the fingerprint of the kernel
+# sources the counters were taken on. A figure whose sources have changed
+# since is not reported (traffic: null).
+# qwen_decode: k_gateup<1,5,2,0> + k_down_combine<1,16,5,true,true>;
+# qwen_layer_decode (no shared expert): k_down_combine<1,16,5,false,true>.
 # deepseek_decode: k_gateup_stream<2,2,false> + k_down_stream_pair<2,2>.
-# deepseek_prefill: every kernel of one moe_expert_prefill call (group,
-# tile_list, quant_mx x2, k_mx_stream gate/up and down, combine).
+# *_prefill: every kernel of one moe_expert_prefill call.
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
-TRAFFIC: dict = {"qwen_decode": 38226594, "deepseek_decode": 114413381, "deepseek_prefill": 7298292121, "fp8_act_quant": 21131081,
-                 "fp8_gemv": 21211008}
+TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
+    "qwen_decode": (38260224, "1b2eeff6fea0269b"),
+    "qwen_layer_decode": (28342989, "1b2eeff6fea0269b"),
+    "deepseek_decode": (114362778, "1b2eeff6fea0269b"),
+    "qwen_prefill": (2806125875, "117daa66577e2462"),
+    "deepseek_prefill": (7298235904, "117daa66577e2462"),
+    "fp8_act_quant": (21129011, "3e24836c4e0819a4"),
+    "fp8_gemv": (21209702, "3e24836c4e0819a4"),
+}
+TRAFFIC_SOURCES = {  # kernel sources behind each workload's figure
+    "decode": ["kernels_decode.hip", "moe_device.h", "moe_internal.h"],
+    "prefill": ["kernels_prefill.hip", "moe_device.h", "moe_internal.h"],
+    "fp8": ["kernels_fp8.hip", "moe_device.h", "moe_internal.h"],
+}
+
+
+def sources_fingerprint(kind: str) -> str:
+    """sha256 (first 16 hex digits) of the kernel sources of a workload kind."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kind]:
+        with open(os.path.join(ROOT, "block_scaled_fp4_route_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str, kind: str):
+    """The counted HBM bytes per call if they were taken on the current sources."""
+    t = TRAFFIC.get(workload)
+    if t is None or t[1] != sources_fingerprint(kind):
+        return None
+    return t[0]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def phase_marker(torch):
+    """A tiny, uniquely named kernel (torch's spin kernel) that separates the
+    phases of a --profile-run in a rocprofv3 trace."""
+    torch.cuda._sleep(100)
 
 
 def log(*a):
@@ -120,34 +169,43 @@ def bytes_per_layer(wl):
     return experts, router, shared, act
 
 
-def cpu_baseline_decode(sg, wl, model, budget_s=20.0):
+def cpu_baseline_decode(sg, wl, model, budget_s=20.0, budget_1t_s=8.0):
     """The oracle on a bounded sample: the first layers of one token, with all
-    host cores, inputs copied to the host before the timer starts."""
+    host cores, then with one thread; inputs copied to the host before the
+    timer starts."""
     import numpy as np
     import torch
     from oracle import oracle as O
     O.build(force=False)
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    nthreads = max(1, cores)
     L = wl.layers
     x = [sg.activations(wl, 0, l, T=1).numpy().reshape(-1) for l in range(L)]
     Wr = [model.Wr[l].cpu().numpy() for l in range(L)]
     sh = [None if s is None else [t.view(torch.int16).cpu().numpy().view(np.uint16) for t in s]
           for s in model.shared[:L]]
-    done, t_total = 0, 0.0
-    while done < L and t_total < budget_s:
-        l = done
-        _, oi, ow = O.route(x[l], Wr[l], wl.k)
-        blks = [model.blocks[l * wl.E + int(e)].cpu().numpy() for e in oi[0]]
-        t0 = time.perf_counter()
-        O.route(x[l], Wr[l], wl.k)
-        O.moe_decode(wl.fmt, wl.H, wl.I, x[l], blks, ow[0], shared=sh[l], nthreads=nthreads)
-        t_total += time.perf_counter() - t0
-        done += 1
-    per_token = t_total / done * L
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"layers 0..{done - 1} of token 0 ({done} of {L} layers, each: fp64 router + "
-                      f"{wl.k} experts + shared), timed {t_total:.1f} s, extrapolated to {L} layers"}
+
+    def run(nthreads, budget):
+        done, t_total = 0, 0.0
+        while done < L and (done == 0 or t_total < budget):
+            l = done
+            _, oi, ow = O.route(x[l], Wr[l], wl.k)
+            blks = [model.blocks[l * wl.E + int(e)].cpu().numpy() for e in oi[0]]
+            t0 = time.perf_counter()
+            O.route(x[l], Wr[l], wl.k)
+            O.moe_decode(wl.fmt, wl.H, wl.I, x[l], blks, ow[0], shared=sh[l], nthreads=nthreads)
+            t_total += time.perf_counter() - t0
+            done += 1
+        return 1.0 / (t_total / done * L), done, t_total
+
+    v, done, t = run(max(1, cores), budget_s)
+    v1, done1, t1 = run(1, budget_1t_s)
+    what = f"fp64 router + {wl.k} experts" + (" + shared" if wl.shared else "")
+    return {"value": v, "unit": "tokens/s", "cores": max(1, cores), "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"layers 0..{done - 1} of token 0 ({done} of {L} layers, each: {what}), "
+                      f"timed {t:.1f} s, extrapolated to {L} layers",
+            "value_1_thread": v1,
+            "sample_1_thread": f"layers 0..{done1 - 1} of token 0 on one thread, timed {t1:.1f} s, "
+                               f"extrapolated to {L} layers"}
 
 
 def run_decode(args, m, sg, torch):
@@ -186,11 +244,15 @@ def run_decode(args, m, sg, torch):
         torch.cuda.current_stream().wait_stream(cs)
         g.replay()  # one untimed replay
         torch.cuda.synchronize()
+        if args.profile_run:
+            phase_marker(torch)
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         mode = "hip_graph"
+        if args.profile_run:
+            phase_marker(torch)
 
     # Per-call durations with HIP events on the launch stream. The calls are
     # enqueued behind a replay of the whole step graph (or a run of eager
@@ -205,6 +267,8 @@ def run_decode(args, m, sg, torch):
         else:
             for s in range(W, W + K):
                 step(s)
+        if args.profile_run:
+            phase_marker(torch)  # the calls that follow are the trace's probe phase
         for i in range(nprobe):
             l = i % wl.layers
             li = (i % nrep) * wl.layers + l if nrep > 1 else l
@@ -215,7 +279,10 @@ def run_decode(args, m, sg, torch):
         return [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
 
     expert_samples = probe(model.experts, ev_x)
-    layer_samples = probe(model.layer, ev_l)
+    if args.profile_run:
+        phase_marker(torch)
+        torch.cuda.synchronize()
+    layer_samples = probe(model.layer, ev_l) if not args.profile_run else expert_samples
     expert_us = statistics.median(expert_samples)
     layer_us_call = statistics.median(layer_samples)
 
@@ -226,7 +293,7 @@ def run_decode(args, m, sg, torch):
     step_bytes = layer_bytes * wl.layers
     expert_call_bytes = experts + shared + act
     achieved = expert_call_bytes / (expert_us * 1e-6) / 1e9
-    copy_gbps = measure_copy_bandwidth(torch)
+    copy_gbps = measure_copy_bandwidth(torch) if not args.profile_run else 0.0
     pair = "k_gateup + k_down_combine" if wl.fmt == "nvfp4" else "k_gateup_stream + k_down_stream_pair"
     res = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -237,7 +304,7 @@ def run_decode(args, m, sg, torch):
                    "tokens_per_step": 1, "replicas": replicas, "launch": mode, "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "expert GEMV: moe_expert_decode (" + pair + ")", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": TRAFFIC.get(wl.name),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(wl.name, "decode"),
                      "bytes_per_launch": expert_call_bytes, "median_us": round(expert_us, 3),
                      "mean_us": round(statistics.fmean(expert_samples), 3), "samples": nprobe},
         "layer_us": round(ms_per_step * 1e3 / wl.layers, 3),
@@ -246,7 +313,9 @@ def run_decode(args, m, sg, torch):
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "hbm_copy_GBps_measured": round(copy_gbps, 1),
     }
-    if not args.no_cpu_baseline:
+    if args.profile_run:
+        res["profile_run"] = True
+    elif not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(sg, wl, model)
     return res
 
@@ -262,23 +331,30 @@ def prefill_flops_bytes(wl, idx, out_bf16):
     return flops, byts, touched
 
 
-def cpu_baseline_prefill(sg, wl, blocks, x, idx, w, budget_tokens=16):
+def cpu_baseline_prefill(sg, wl, blocks, x, idx, w, budget_tokens=16, tokens_1t=4):
     import numpy as np
     from oracle import oracle as O
     O.build(force=False)
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    toks = np.linspace(0, wl.T - 1, budget_tokens).astype(int)
-    ih = idx.cpu().numpy()[toks]
-    hb = {int(e): blocks[int(e)].cpu().numpy() for e in np.unique(ih)}
-    xh = x.cpu().numpy()[toks]
-    wh = w.cpu().numpy()[toks]
-    t0 = time.perf_counter()
-    O.moe_prefill(wl.fmt, wl.H, wl.I, wl.E, xh, hb, ih, wh, act=1 if wl.fmt == "nvfp4" else 2,
-                  out_bf16=wl.out_bf16, nthreads=cores)
-    dt = time.perf_counter() - t0
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(toks)} of {wl.T} prompt tokens (evenly spaced) through the layer with their "
-                      f"{wl.k} experts each, fp64, one thread per token, timed {dt:.1f} s"}
+
+    def run(ntok, nthreads):
+        toks = np.linspace(0, wl.T - 1, ntok).astype(int)
+        ih = idx.cpu().numpy()[toks]
+        hb = {int(e): blocks[int(e)].cpu().numpy() for e in np.unique(ih)}
+        xh = x.cpu().numpy()[toks]
+        wh = w.cpu().numpy()[toks]
+        t0 = time.perf_counter()
+        O.moe_prefill(wl.fmt, wl.H, wl.I, wl.E, xh, hb, ih, wh, act=1 if wl.fmt == "nvfp4" else 2,
+                      out_bf16=wl.out_bf16, nthreads=nthreads)
+        return len(toks), time.perf_counter() - t0
+
+    n, dt = run(budget_tokens, cores)
+    n1, dt1 = run(tokens_1t, 1)
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{n} of {wl.T} prompt tokens (evenly spaced) through the layer with their "
+                      f"{wl.k} experts each, fp64, one thread per token, timed {dt:.1f} s",
+            "value_1_thread": n1 / dt1,
+            "sample_1_thread": f"{n1} of {wl.T} prompt tokens on one thread, timed {dt1:.1f} s"}
 
 
 def run_prefill(args, m, sg, torch):
@@ -297,15 +373,27 @@ def run_prefill(args, m, sg, torch):
     log(f"[bench] {wl.name}: {wl.E} experts resident ({blocks.numel() / 2**30:.2f} GiB), "
         f"{wl.T} tokens, set up in {time.time() - t0:.1f} s")
     K, W = args.steps, args.warmup
-    for _ in range(W):
+    # warmup: at least W calls and at least 0.5 s of them (a few calls leave
+    # the GPU short of its steady clocks: 3 calls after 3 warmup calls time
+    # 20% slower than calls after half a second of work)
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < W or time.perf_counter() - t_w < 0.5:
         m.moe_expert_prefill(d, x, wl.T, ptrs, idx, w, out, od, ws)
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    if args.profile_run:
+        phase_marker(torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(K):
         m.moe_expert_prefill(d, x, wl.T, ptrs, idx, w, out, od, ws)
     e1.record()
     torch.cuda.synchronize()
+    if args.profile_run:
+        phase_marker(torch)
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     flops, byts, touched = prefill_flops_bytes(wl, idx, wl.out_bf16)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -313,7 +401,7 @@ def run_prefill(args, m, sg, torch):
     mfma_peak = 2500.0 if wl.fmt == "nvfp4" else 10100.0
     res = {
         "metric": METRIC, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "warmup": n_w, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 MFMA, f32 accumulate" if wl.fmt == "nvfp4" else "mxfp4 MFMA, f32 accumulate",
         "data": "synthetic (seeded SplitMix64; random-code FP4 experts, no trained weights)",
         "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "intermediate": wl.I,
@@ -322,12 +410,18 @@ def run_prefill(args, m, sg, torch):
                    "out": "bf16" if wl.out_bf16 else "f32", "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "moe_expert_prefill (grouping + quantise + grouped GEMMs + combine)",
                      "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": TRAFFIC.get(wl.name), "bytes_per_launch": int(byts),
-                     "avg_us": round(ms * 1e3, 2)},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(wl.name, "prefill"),
+                     "bytes_per_launch": int(byts), "avg_us": round(ms * 1e3, 2)},
         "mfma_TFLOPs": round(tflops, 2), "mfma_peak_TFLOPs": mfma_peak,
         "mfma_frac": round(tflops / mfma_peak, 4), "flops_per_call": flops,
+        # the fp32 expert outputs Y [assignments][H], written by the down GEMM
+        # and read back by the combine: bytes beyond the algorithmic ones
+        "y_round_trip": {"bytes": 2 * int(idx.numel()) * wl.H * 4,
+                         "share_of_algorithmic": round(2 * int(idx.numel()) * wl.H * 4 / byts, 4)},
     }
-    if not args.no_cpu_baseline:
+    if args.profile_run:
+        res["profile_run"] = True
+    elif not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(sg, wl, blocks, x, idx, w)
     return res
 
@@ -388,11 +482,16 @@ def run_fp8(args, m, sg, torch):
     torch.cuda.current_stream().wait_stream(cs)
     g.replay()
     torch.cuda.synchronize()
+    if args.profile_run:
+        phase_marker(torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     g.replay()
     e1.record()
     torch.cuda.synchronize()
+    if args.profile_run:
+        phase_marker(torch)
+        torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / K
     gbps = nbytes / (us * 1e-6) / 1e9
     res = {
@@ -404,7 +503,7 @@ def run_fp8(args, m, sg, torch):
         "config": {"workload": args.workload, **cfg, "replicas": nrep, "launch": "hip_graph",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": TRAFFIC.get(args.workload),
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(args.workload, "fp8"),
                      "bytes_per_launch": nbytes, "avg_us": round(us, 3)},
     }
     if not args.no_cpu_baseline:
@@ -624,6 +723,59 @@ def run_speculate(args, m, sg, torch):
     return res
 
 
+def summarize(root: str) -> None:
+    """Per-phase kernel tables from rocprofv3 CSV output (kernel trace or
+    counter collection) of a --profile-run: the phases are the intervals
+    between the marker kernels (phase 1: the timed region; decode phase 3: the
+    expert-call probes); a run without markers is one phase."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True) +
+                   glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        print(f"no rocprofv3 CSV under {root}")
+        return
+    for fn in files:
+        disp = {}  # dispatch id -> [name, start, end, {counter: value}]
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                d = disp.setdefault(r["Dispatch_Id"], [r["Kernel_Name"], int(r["Start_Timestamp"]),
+                                                       int(r["End_Timestamp"]), {}])
+                if "Counter_Name" in r:
+                    d[3][r["Counter_Name"]] = d[3].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        rows = sorted(disp.values(), key=lambda d: d[1])
+        marks = [d[1] for d in rows if "spin_kernel" in d[0]]
+        bounds = list(zip(marks, marks[1:])) if len(marks) >= 2 else [(rows[0][1] - 1, rows[-1][2] + 1)]
+        outside = sum(1 for d in rows if not any(lo < d[1] < hi for lo, hi in bounds))
+        print(f"### {os.path.relpath(fn, root)}\n")
+        print(f"{len(marks)} phase markers; {outside} dispatches outside the phases (set-up, warmup)\n")
+        for ph, (lo, hi) in enumerate(bounds, 1):
+            sel = [d for d in rows if lo < d[1] < hi and "spin_kernel" not in d[0]]
+            if not sel:
+                continue
+            by = {}
+            for d in sel:
+                by.setdefault(d[0], []).append(d)
+            counters = sorted({c for d in sel for c in d[3]})
+            print(f"phase {ph}: {len(sel)} dispatches, {(max(d[2] for d in sel) - min(d[1] for d in sel)) / 1e3:.1f} us "
+                  f"first start to last end\n")
+            if counters:
+                print("| kernel | dispatches | " + " | ".join(f"{c} (mean)" for c in counters) + " |")
+                print("|---|---|" + "---|" * len(counters))
+            else:
+                print("| kernel | dispatches | avg us | min us | max us | total us |")
+                print("|---|---|---|---|---|---|")
+            for name, ds in sorted(by.items(), key=lambda kv: -sum(d[2] - d[1] for d in kv[1])):
+                if counters:
+                    vals = [statistics.fmean([d[3].get(c, 0.0) for d in ds]) for c in counters]
+                    print(f"| `{name[:90]}` | {len(ds)} | " + " | ".join(f"{v:,.1f}" for v in vals) + " |")
+                else:
+                    us = [(d[2] - d[1]) / 1e3 for d in ds]
+                    print(f"| `{name[:90]}` | {len(ds)} | {statistics.fmean(us):.2f} | {min(us):.2f} | "
+                          f"{max(us):.2f} | {sum(us):.1f} |")
+            print()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -638,9 +790,18 @@ def main():
     ap.add_argument("--tier-promote", type=int, default=16, help="qwen_tier: promotions per token at most")
     ap.add_argument("--tier-hot", type=int, default=48, help="qwen_tier: hot experts per layer (skewed run)")
     ap.add_argument("--tier-hot-scale", type=float, default=3.0, help="qwen_tier: router scale of hot experts")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="for rocprofv3: marker kernels around the timed region (phase 1) and, in a decode "
+                         "run, around the expert-call probes (phase 3, after the replay that precedes them); "
+                         "no copy-bandwidth probe and no CPU baseline")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print per-phase kernel tables from the rocprofv3 CSVs under DIR (no GPU needed)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 4 device copies of 1 GiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path, and each "
               "step computes the whole MoE layer on that GPU.", file=sys.stderr)
