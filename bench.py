@@ -45,10 +45,10 @@ TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
     "qwen_decode": (38260224, "1b2eeff6fea0269b"),
     "qwen_layer_decode": (28342989, "1b2eeff6fea0269b"),
     "deepseek_decode": (114362778, "1b2eeff6fea0269b"),
-    "qwen_prefill": (2806125875, "117daa66577e2462"),
-    "deepseek_prefill": (7298235904, "117daa66577e2462"),
-    "fp8_act_quant": (21129011, "3e24836c4e0819a4"),
-    "fp8_gemv": (21209702, "3e24836c4e0819a4"),
+    "qwen_prefill": (2806496563, "117daa66577e2462"),
+    "deepseek_prefill": (7297880371, "117daa66577e2462"),
+    "fp8_act_quant": (21128192, "3e24836c4e0819a4"),
+    "fp8_gemv": (21209088, "3e24836c4e0819a4"),
 }
 TRAFFIC_SOURCES = {  # kernel sources behind each workload's figure
     "decode": ["kernels_decode.hip", "moe_device.h", "moe_internal.h"],
