@@ -543,8 +543,9 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
     constexpr int PASSES = kDownRB / (64 / DL);
     const int tid = threadIdx.x, wave = wave_id(), nwaves = blockDim.x >> 6;
     const int rb = blockIdx.x, k = a.k;
-    // the combine's weights, requested while the weights stream
-    if (tid < k) wsh[tid] = a.w[tid];
+    // the combine's weights: loaded now, stored to LDS after the items (a
+    // store here would hold wave 0's weight loads behind this load)
+    const float wt = a.w[min(tid, k - 1)];
     if constexpr (PAIRS) {
         // one unit per wave: kDownNJ routed items (items w, w + npair, ...),
         // then the two halves of the shared expert's rows; the wave's kDownNJ
@@ -577,6 +578,7 @@ __global__ __launch_bounds__(64 * down_max_waves(DL, DD)) void k_down_combine(De
                                                  hs);
         }
     }
+    if (tid < k) wsh[tid] = wt;
     __syncthreads();
     if (tid < kDownRB) {
         const int row = rb * kDownRB + tid;
