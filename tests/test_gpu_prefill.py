@@ -154,10 +154,10 @@ def summary(name, rec):
             json.dump(rec, f, indent=1)
 
 
-def full_check(m, orc, wl, T, seed_layer=0, sample=None, tag=None):
+def full_check(m, orc, wl, T, seed_layer=0, sample=None, tag=None, routing=None):
     blocks = layer_blocks(wl, seed_layer)
     x = sg.activations(wl, 0, seed_layer, T=T, device="cuda")
-    idx, w = sg.routing(wl, T=T, layer=seed_layer)
+    idx, w = sg.routing(wl, T=T, layer=seed_layer) if routing is None else routing
     g = run_gpu(m, wl, blocks, x, idx.cuda(), w.cuda(), False)
     k, I, H = wl.k, wl.I, wl.H
     # grouping: bit-exact
@@ -281,6 +281,32 @@ def test_prefill_nvfp4_down_scale_staging(m, orc, H, I, E, k, T):
     I = 1024 (256 rows x 64 scale bytes) and loads them per chunk above it:
     both forms, with tiles of more than one row block."""
     full_check(m, orc, wl_small("nvfp4", H, I, E, k, T), T)
+
+
+def counts_routing(counts, T):
+    """Routing with exactly counts[e] assignments to expert e over T tokens of
+    k = 2 (two distinct experts per token: slot 0 takes the first T expert
+    ids in expert order, slot 1 the rest; no count exceeds T), weights from a
+    seeded generator."""
+    ids = np.repeat(np.arange(len(counts)), counts)
+    assert ids.size == 2 * T and max(counts) <= T
+    idx = np.stack([ids[:T], ids[T:]], axis=1).astype(np.int32)
+    assert (idx[:, 0] != idx[:, 1]).all()
+    z = np.random.default_rng(7).standard_normal((T, 2))
+    w = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
+    return torch.from_numpy(idx), torch.from_numpy(w.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_prefill_tile_row_counts(m, orc, fmt):
+    """Experts with exactly 1, 16, 17, 32, 33, 64, 65, 127, 128 and 129 rows
+    (plus one of 148): every row-block specialisation of the grouped GEMMs,
+    both NVFP4 tile heights (64 rows up to 64, 128 rows above) and the ragged
+    last tile of a multi-tile expert."""
+    counts = [1, 16, 17, 32, 33, 64, 65, 127, 128, 129, 148]
+    T = sum(counts) // 2
+    wl = wl_small(fmt, 512, 128 if fmt == "nvfp4" else 64, len(counts), 2, T)
+    full_check(m, orc, wl, T, routing=counts_routing(counts, T), tag=f"tile_row_counts_{fmt}")
 
 
 def test_prefill_mxfp4_deepseek_shape_small_E(m, orc):
