@@ -42,9 +42,9 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # *_prefill: every kernel of one moe_expert_prefill call.
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
 TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
-    "qwen_decode": (38260224, "1b2eeff6fea0269b"),
-    "qwen_layer_decode": (28342989, "1b2eeff6fea0269b"),
-    "deepseek_decode": (114362778, "1b2eeff6fea0269b"),
+    "qwen_decode": (38256128, "c8830d685473043a"),
+    "qwen_layer_decode": (28344013, "c8830d685473043a"),
+    "deepseek_decode": (114377728, "c8830d685473043a"),
     "qwen_prefill": (2806496563, "117daa66577e2462"),
     "deepseek_prefill": (7297880371, "117daa66577e2462"),
     "fp8_act_quant": (21128192, "3e24836c4e0819a4"),
