@@ -45,8 +45,8 @@ TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
     "qwen_decode": (38256128, "c8830d685473043a"),
     "qwen_layer_decode": (28344013, "c8830d685473043a"),
     "deepseek_decode": (114377728, "c8830d685473043a"),
-    "qwen_prefill": (2806496563, "117daa66577e2462"),
-    "deepseek_prefill": (7297880371, "117daa66577e2462"),
+    "qwen_prefill": (2746399642, "bbc62890b92fc7c3"),
+    "deepseek_prefill": (7282899968, "bbc62890b92fc7c3"),
     "fp8_act_quant": (21128192, "3e24836c4e0819a4"),
     "fp8_gemv": (21209088, "3e24836c4e0819a4"),
 }
@@ -402,7 +402,7 @@ def run_prefill(args, m, sg, torch):
     res = {
         "metric": METRIC, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": n_w, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 MFMA, f32 accumulate" if wl.fmt == "nvfp4" else "mxfp4 MFMA, f32 accumulate",
+        "dtype": "fp16 (gate/up) and bf16 (down) MFMA, f32 accumulate" if wl.fmt == "nvfp4" else "mxfp4 MFMA, f32 accumulate",
         "data": "synthetic (seeded SplitMix64; random-code FP4 experts, no trained weights)",
         "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "intermediate": wl.I,
                    "weights": wl.fmt, "tokens": wl.T, "assignments": int(idx.numel()), "experts_touched": touched,

@@ -7,13 +7,17 @@
 //     (count, exclusive prefix sum, ordered compaction with ballots:
 //     deterministic, no atomics).
 //  2. k_tile_list: M-tiles of every expert, heaviest experts first.
-//  3. k_quant_x_*: x~ = bf16(x) (NVFP4 layers) or MXFP4 per 32 (MXFP4 layers).
+//  3. k_quant_*: x~ = bf16(x) (NVFP4 layers; held for the GEMM as fp16 times
+//     a power of two per token, exactly) or MXFP4 per 32 (MXFP4 layers).
 //  4. ragged grouped GEMMs (gate/up with SiLU*mul epilogue, then down):
-//     NVFP4 weights are decoded to bf16 in registers and multiplied with
-//     v_mfma_f32_16x16x32_bf16; MXFP4 weights (streamed through an LDS ring)
+//     NVFP4 weights are decoded in registers, exactly, to fp16 for gate/up
+//     (v_mfma_f32_16x16x32_f16) and to bf16 for down against h~
+//     (v_mfma_f32_16x16x32_bf16); MXFP4 weights (streamed through an LDS ring)
 //     and activations go straight into v_mfma_scale_f32_16x16x128_f8f6f4
 //     with their E8M0 scales.
 //  5. k_combine: out[t] = sum_j w[t][j] * Y[pos(t, j)] in increasing j.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -25,6 +29,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBM_NV = 64;    // NVFP4 M-tile (rows of one expert)
 constexpr int kBM_NV2 = 128;  // NVFP4 M-tile of the heavy experts
@@ -43,7 +49,8 @@ struct PrefillWs {
     int* tile_m;  // [max_tiles] first row of the tile within its expert
     int* ntiles;  // [1]
     void* rec;    // [max_tiles] TileRec (MXFP4 GEMMs)
-    void* xq;     // x~: bf16 [T][H] | MXFP4 codes [T][H/2] + scales [T][H/32]
+    void* xq;     // x~: scaled fp16 [T][H] | MXFP4 codes [T][H/2] + scales [T][H/32]
+    int* xexp;    // NVFP4: [T] power-of-two exponent of each row of the fp16 x~
     void* hq;     // h~: bf16 [T*k][I] | MXFP4 codes [T*k][I/2] + scales [T*k][I/32]
     float* hf;    // MXFP4 only: h before rounding [T*k][I]
     float* Y;     // [T*k][H]
@@ -72,6 +79,7 @@ static PrefillWs prefill_layout(int fmt, int H, int I, int E, int k, int T, void
     w.rec = take(16 * (size_t)mt);
     if (fmt == kFmtNvfp4) {
         w.xq = take((size_t)T * H * 2);
+        w.xexp = (int*)take(sizeof(int) * (size_t)T);
         w.hq = take(n * I * 2);
         w.hf = nullptr;
     } else {
@@ -318,16 +326,71 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
 // ---------------------------------------------------------------------------
 // 3. activation rounding
 
-// x~ = bf16(x), round to nearest even (v_cvt_pk_bf16_f32); 8 values per thread.
-__global__ __launch_bounds__(256) void k_quant_bf16(const float* __restrict__ x, size_t n8, bf16x8* __restrict__ out) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a = reinterpret_cast<const f32x4*>(x)[2 * i], b = reinterpret_cast<const f32x4*>(x)[2 * i + 1];
-    const f32x2 p0 = {a.x, a.y}, p1 = {a.z, a.w}, p2 = {b.x, b.y}, p3 = {b.z, b.w};
-    const bf16x2 q0 = __builtin_convertvector(p0, bf16x2), q1 = __builtin_convertvector(p1, bf16x2);
-    const bf16x2 q2 = __builtin_convertvector(p2, bf16x2), q3 = __builtin_convertvector(p3, bf16x2);
-    bf16x8 o = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-    out[i] = o;
+// NVFP4 layers: x~ = bf16(x) (round to nearest even), handed to the gate/up
+// GEMM as fp16 times a power of two per token: one wave per row finds
+// m = the largest finite |x~| of the row and picks t with m * 2^t in
+// [2^14, 2^15) (t = 0 for a row with no nonzero finite value). Every bf16
+// value of the row with |x~| * 2^t >= 2^-14 is then an fp16 normal and
+// converts exactly (8 significant bits into 11), and nothing overflows; the
+// GEMM multiplies its sums by 2^-t. Only values more than 2^28 below the
+// row's largest can lose bits (fp16 subnormals), a change of at most 2^-25 of
+// the row maximum per element. Non-finite values pass through. The bf16
+// values themselves go to xdbg when it is given.
+// One wave per row, the row read twice (the second pass from L2) in blocks
+// of 16 float4 per lane whose loads are all issued before the first use.
+constexpr int kQuantBlk = 16;
+__global__ __launch_bounds__(256) void k_quant_f16(const float* __restrict__ x, int T, int H, f16x2* __restrict__ out,
+                                                   int* __restrict__ xexp, bf16x2* __restrict__ xdbg) {
+    const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + wave_id(), H4 = H / 4;
+    if (row >= T) return;
+    const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)row * H);
+    auto to_bf16 = [](const f32x4 a, bf16x2& q0, bf16x2& q1) {
+        const f32x2 p0 = {a.x, a.y}, p1 = {a.z, a.w};
+        q0 = __builtin_convertvector(p0, bf16x2);
+        q1 = __builtin_convertvector(p1, bf16x2);
+    };
+    float m = 0.f;
+    for (int b0 = 0; b0 < H4; b0 += 64 * kQuantBlk) {
+        f32x4 v[kQuantBlk];
+#pragma unroll
+        for (int u = 0; u < kQuantBlk; u++) v[u] = xr[min(b0 + lane + 64 * u, H4 - 1)];
+#pragma unroll
+        for (int u = 0; u < kQuantBlk; u++) {
+            bf16x2 q0, q1;
+            to_bf16(v[u], q0, q1);
+            const float a[4] = {fabsf((float)q0.x), fabsf((float)q0.y), fabsf((float)q1.x), fabsf((float)q1.y)};
+#pragma unroll
+            for (int c = 0; c < 4; c++) m = a[c] <= 3.4028235e38f ? fmaxf(m, a[c]) : m;  // finite only (NaN: false)
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    int e = 0;
+    if (m > 0.f) frexpf(m, &e);  // m in [2^(e-1), 2^e)
+    const int t = m > 0.f ? 15 - e : 0;
+    if (lane == 0) xexp[row] = t;
+    f16x2* o = out + (size_t)row * (H / 2);
+    for (int b0 = 0; b0 < H4; b0 += 64 * kQuantBlk) {
+        f32x4 v[kQuantBlk];
+#pragma unroll
+        for (int u = 0; u < kQuantBlk; u++) v[u] = xr[min(b0 + lane + 64 * u, H4 - 1)];
+#pragma unroll
+        for (int u = 0; u < kQuantBlk; u++) {
+            const int i = b0 + lane + 64 * u;
+            if (i < H4) {
+                bf16x2 q0, q1;
+                to_bf16(v[u], q0, q1);
+                if (xdbg) {
+                    xdbg[(size_t)row * (H / 2) + 2 * i] = q0;
+                    xdbg[(size_t)row * (H / 2) + 2 * i + 1] = q1;
+                }
+                const f32x2 p0 = {ldexpf((float)q0.x, t), ldexpf((float)q0.y, t)};
+                const f32x2 p1 = {ldexpf((float)q1.x, t), ldexpf((float)q1.y, t)};
+                o[2 * i] = __builtin_convertvector(p0, f16x2);
+                o[2 * i + 1] = __builtin_convertvector(p1, f16x2);
+            }
+        }
+    }
 }
 
 // e2m1 code of |t| (t already divided by the block scale, exact), ties to
@@ -387,7 +450,7 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
 }
 
 // ---------------------------------------------------------------------------
-// 4a. NVFP4 gate/up: ragged grouped GEMM with bf16 MFMA.
+// 4a. NVFP4 gate/up: ragged grouped GEMM with fp16 MFMA.
 //
 // Workgroup = (M-tile of one expert, 128 output columns of I). M-tiles are
 // 128 rows for the experts that have more than 64 rows and 64 rows for the
@@ -400,8 +463,12 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
 // the 128-row tiles, whose A tile then takes the same LDS); within a
 // chunk each lane group owns a contiguous quarter of K (see nv_kloop), with
 // the A operand read from LDS under the same K mapping (the dot product is
-// order-independent). The codes are decoded to bf16 exactly (e2m1 x E4M3 has
-// at most 6 significant bits).
+// order-independent). The codes are decoded to fp16 exactly (e2m1 x E4M3 has
+// at most 6 significant bits and lies in the fp16 normal range); fp16 takes
+// two instructions per two codes (conversion, packed multiply) where bf16
+// takes four, since the hardware conversion applies only the exponent of a
+// scale and gfx950 has no packed bf16 multiply. x~ comes as fp16 times 2^t
+// per token (k_quant_f16), and the epilogue multiplies the sums by 2^-t.
 // Workgroup -> (M-tile, N-tile). Workgroups are dispatched round-robin over
 // the 8 XCDs (each with its own L2), so workgroup b runs on XCD b % 8. M-tile
 // t goes to XCD t % 8 and all NT N-tiles of an M-tile (the same gathered
@@ -432,6 +499,7 @@ struct GemmArgs {
     int E, H, I, k, NT;     // NT = N-tiles per M-tile
     uint32_t a_bytes;       // bytes of a_src
     uint32_t a_scl_bytes;   // bytes of a_scl (MXFP4)
+    const int* xexp;        // NVFP4 gate/up: per-token exponent of the fp16 x~
     uint32_t block_bytes;   // bytes of one expert block
     const TileRec* rec;     // MXFP4: tile records
     int mt;                 // MXFP4: record slots
@@ -448,6 +516,19 @@ template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Decode 8 e2m1 codes (dword d) times scale s to 8 fp16 (exact: a code has
+// at most 2 significant bits and an E4M3 scale 4, and |code * scale| lies in
+// [2^-10, 2688], inside the fp16 normal range).
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t d, _Float16 s) {
+    const f16x2 ss = {s, s};
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * ss;
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * ss;
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * ss;
+    const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * ss;
+    f16x8 o = {a.x, a.y, b.x, b.y, c.x, c.y, e.x, e.y};
+    return o;
 }
 
 // Decode 8 e2m1 codes (dword d) times scale s to 8 bf16 (exact).
@@ -498,7 +579,7 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off)
 // code that uses a or b after it cannot be scheduled before it.
 __device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
-template <int BK, int RB, int MR, bool SL, class AROW>
+template <int BK, int RB, int MR, bool SL, bool F16, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
                                          uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
@@ -589,11 +670,13 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
                 // the A fragments of all row blocks first (the MR-row tile is
                 // always allocated), so their LDS latency hides behind the decode
                 const int p = (QK / 8) * g + s;  // 16-byte piece of the fragment
-                bf16x8 af[RB];
+                // fragments as 16-byte vectors of the operand type
+                typedef std::conditional_t<F16, f16x8, bf16x8> opv;
+                opv af[RB];
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++) {
                     const int r = 16 * rb + m16;
-                    af[rb] = *reinterpret_cast<const bf16x8*>(At + (r * SPR + (p ^ (r & 7))) * 8);
+                    af[rb] = *reinterpret_cast<const opv*>(At + (r * SPR + (p ^ (r & 7))) * 8);
                 }
                 // no branches inside a chunk: the MFMAs of column block cb can
                 // issue between the decode instructions of block cb+1
@@ -602,10 +685,17 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
                     const uint4 q = bc[cb][s / 4];
                     const uint32_t d = (s & 3) == 0 ? q.x : ((s & 3) == 1 ? q.y : ((s & 3) == 2 ? q.z : q.w));
                     const float sv = e4m3_to_f32((sc[cb] >> (8 * (s / 2))) & 0xFFu);
-                    const bf16x8 bf = dequant8_bf16(d, sv);
+                    if constexpr (F16) {
+                        const f16x8 bf = dequant8_f16(d, (_Float16)sv);
 #pragma unroll
-                    for (int rb = 0; rb < RB; rb++)
-                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rb], bf, acc[rb][cb], 0, 0, 0);
+                        for (int rb = 0; rb < RB; rb++)
+                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb], bf, acc[rb][cb], 0, 0, 0);
+                    } else {
+                        const bf16x8 bf = dequant8_bf16(d, sv);
+#pragma unroll
+                        for (int rb = 0; rb < RB; rb++)
+                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rb], bf, acc[rb][cb], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -645,20 +735,27 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
     for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<BK, RB, MR, false>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H, lds,
-                                nullptr, 0);
-    // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i
+    nv_kloop<BK, RB, MR, false, true>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H,
+                                      lds, nullptr, 0);
+    // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i;
+    // the sums carry the row's 2^t of the fp16 x~ (exact to undo)
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
-    for (int rb = 0; rb < RB; rb++)
+    for (int rb = 0; rb < RB; rb++) {
+        int nt_[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = 16 * rb + 4 * g + i;
+            nt_[i] = -a.xexp[perm[base + min(r, rows - 1)] / k];
+        }
 #pragma unroll
         for (int cbg = 0; cbg < 2; cbg++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int r = 16 * rb + 4 * g + i;
                 if (r < rows) {
-                    const float hv = silu_mul(acc[rb][cbg][i], acc[rb][cbg + 2][i]);
+                    const float hv = silu_mul(ldexpf(acc[rb][cbg][i], nt_[i]), ldexpf(acc[rb][cbg + 2][i], nt_[i]));
                     const __bf16 hb = (__bf16)hv;
                     const size_t o = (size_t)(base + r) * I + c0 + 16 * cbg + m16;
                     hq[o] = hb;
@@ -666,6 +763,7 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
                     if (a.h_q) a.h_q[o] = (float)hb;
                 }
             }
+    }
 }
 
 // Rows of tile (e, m0): tiles are kBM_NV2 rows high for experts with at least
@@ -721,7 +819,7 @@ __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, con
     for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<kBKDown, RB, MR, SL>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds,
+    nv_kloop<kBKDown, RB, MR, SL, false>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds,
                                   sl, nt * 256);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
@@ -1123,12 +1221,11 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     ga.h_pre = dbg ? dbg->h_pre : nullptr;
 
     if (fmt == kFmtNvfp4) {
-        __bf16* xq = dbg && dbg->x_bf16 ? reinterpret_cast<__bf16*>(dbg->x_bf16) : reinterpret_cast<__bf16*>(L.xq);
-        const size_t n8 = (size_t)T * H / 8;
-        hipLaunchKernelGGL(k_quant_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, n8,
-                           reinterpret_cast<bf16x8*>(xq));
+        hipLaunchKernelGGL(k_quant_f16, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, reinterpret_cast<f16x2*>(L.xq), L.xexp,
+                           dbg && dbg->x_bf16 ? reinterpret_cast<bf16x2*>(dbg->x_bf16) : (bf16x2*)nullptr);
         LAUNCH_CHECK();
-        ga.a_src = xq; ga.out = L.hq; ga.h_q = dbg ? dbg->h_q : nullptr; ga.NT = I / 128;
+        ga.a_src = L.xq;
+        ga.xexp = L.xexp; ga.out = L.hq; ga.h_q = dbg ? dbg->h_q : nullptr; ga.NT = I / 128;
         ga.a_bytes = (uint32_t)((size_t)T * H * 2);
         ga.block_bytes = (uint32_t)((size_t)3 * H * I / 2 + (size_t)3 * H * I / 16);
         hipLaunchKernelGGL(k_gateup_nv, dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
