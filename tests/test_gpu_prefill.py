@@ -154,9 +154,10 @@ def summary(name, rec):
             json.dump(rec, f, indent=1)
 
 
-def full_check(m, orc, wl, T, seed_layer=0, sample=None, tag=None, routing=None):
+def full_check(m, orc, wl, T, seed_layer=0, sample=None, tag=None, routing=None, x=None):
     blocks = layer_blocks(wl, seed_layer)
-    x = sg.activations(wl, 0, seed_layer, T=T, device="cuda")
+    if x is None:
+        x = sg.activations(wl, 0, seed_layer, T=T, device="cuda")
     idx, w = sg.routing(wl, T=T, layer=seed_layer) if routing is None else routing
     g = run_gpu(m, wl, blocks, x, idx.cuda(), w.cuda(), False)
     k, I, H = wl.k, wl.I, wl.H
@@ -295,6 +296,25 @@ def counts_routing(counts, T):
     z = np.random.default_rng(7).standard_normal((T, 2))
     w = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
     return torch.from_numpy(idx), torch.from_numpy(w.astype(np.float32))
+
+
+def test_prefill_nvfp4_activation_ranges(m, orc):
+    """The NVFP4 gate/up GEMM takes x~ = bf16(x) as fp16 times a power of two
+    per token. Rows far above and below 1, a row spanning 2^40 from its largest
+    to its smallest element, an all-zero row, a row with one nonzero element
+    and a row of largest-magnitude ties stay at the stage-wise bar."""
+    wl = wl_small("nvfp4", 512, 128, 8, 2, 40)
+    T, H = 40, wl.H
+    x = sg.activations(wl, 0, 0, T=T, device="cuda").clone()
+    x[0] *= 2.0 ** 24
+    x[1] *= 2.0 ** -40
+    x[2] *= torch.exp2(-40.0 * torch.arange(H, device="cuda", dtype=torch.float32) / H)
+    x[3] = 0.0
+    x[4] = 0.0
+    x[4, 7] = -3.0
+    x[5] = torch.where(torch.arange(H, device="cuda") % 2 == 0, 1.0, -1.0) * 65504.0
+    x[6, ::3] *= 2.0 ** -30
+    full_check(m, orc, wl, T, x=x, tag="pf_nvfp4_activation_ranges")
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
