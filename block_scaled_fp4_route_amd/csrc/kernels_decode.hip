@@ -786,15 +786,18 @@ __global__ __launch_bounds__(256) void k_gateup_stream(DecodeArgs a) {
             return;
         }
         const int slot = u / I, r = u % I;
+        // every scale permute first, so that one LDS wait covers them all
+        uint32_t scv[2][NCH];
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int m = 0; m < NCH; m++) scv[h][m] = chunk_scale(sw[d], h, min(lane + 64 * m, nchunk - 1));
         float t[2];
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             float acc = 0.f;
 #pragma unroll
-            for (int m = 0; m < NCH; m++) {
-                const int c = min(lane + 64 * m, nchunk - 1);
-                acc = chunk_dot<FMT>(cw[d][h][m], chunk_scale(sw[d], h, c), xs[m], acc);
-            }
+            for (int m = 0; m < NCH; m++) acc = chunk_dot<FMT>(cw[d][h][m], scv[h][m], xs[m], acc);
             t[h] = wave_sum(acc);
         }
         // one store instruction (lanes other than 0 store to an out-of-range
