@@ -42,9 +42,9 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # *_prefill: every kernel of one moe_expert_prefill call.
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
 TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
-    "qwen_decode": (38256128, "c8830d685473043a"),
-    "qwen_layer_decode": (28344013, "c8830d685473043a"),
-    "deepseek_decode": (114377728, "c8830d685473043a"),
+    "qwen_decode": (38256128, "59e88a0decc5560a"),
+    "qwen_layer_decode": (28344013, "59e88a0decc5560a"),
+    "deepseek_decode": (114379776, "59e88a0decc5560a"),
     "qwen_prefill": (2746399642, "bbc62890b92fc7c3"),
     "deepseek_prefill": (7282899968, "bbc62890b92fc7c3"),
     "fp8_act_quant": (21128192, "3e24836c4e0819a4"),
