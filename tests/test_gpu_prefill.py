@@ -298,6 +298,14 @@ def counts_routing(counts, T):
     return torch.from_numpy(idx), torch.from_numpy(w.astype(np.float32))
 
 
+@pytest.mark.parametrize("H,I,E,k,T", [(8192, 256, 4, 2, 9), (16384, 128, 3, 2, 5)])
+def test_prefill_nvfp4_wide_rows(m, orc, H, I, E, k, T):
+    """Rows of 8192 and 16384 values: the activation conversion takes its
+    rows in several blocks per lane, and the gate/up K loop runs 32 and 64
+    chunks."""
+    full_check(m, orc, wl_small("nvfp4", H, I, E, k, T), T)
+
+
 def test_prefill_nvfp4_activation_ranges(m, orc):
     """The NVFP4 gate/up GEMM takes x~ = bf16(x) as fp16 times a power of two
     per token. Rows far above and below 1, a row spanning 2^40 from its largest
