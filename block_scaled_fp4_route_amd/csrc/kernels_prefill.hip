@@ -1163,19 +1163,36 @@ __global__ __launch_bounds__(256) void k_combine_prefill(const float* __restrict
     const int c4 = blockIdx.x * 256 + threadIdx.x;  // float4 column
     if (c4 * 4 >= H) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; j++) {
-        const int p = pos[t * k + j];
-        const float wj = w[t * k + j];
-        if (p < 0) {
-            acc = f32x4{__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
-                        __uint_as_float(0x7FC00000u)};
-            continue;
+    // groups of up to 8 assignments: all their Y loads first, then the sums
+    // in increasing j
+    constexpr int NG = 8;
+    for (int j0 = 0; j0 < k; j0 += NG) {
+        int pv[NG];
+        float wv[NG];
+#pragma unroll
+        for (int i = 0; i < NG; i++) {
+            pv[i] = pos[t * k + min(j0 + i, k - 1)];
+            wv[i] = w[t * k + min(j0 + i, k - 1)];
         }
-        const f32x4 yv = reinterpret_cast<const f32x4*>(Y + (size_t)p * H)[c4];
-        acc.x = fmaf(wj, yv.x, acc.x);
-        acc.y = fmaf(wj, yv.y, acc.y);
-        acc.z = fmaf(wj, yv.z, acc.z);
-        acc.w = fmaf(wj, yv.w, acc.w);
+        __builtin_amdgcn_sched_barrier(0);  // the positions' and weights' loads issue together, before the rows'
+        f32x4 yv[NG];
+#pragma unroll
+        for (int i = 0; i < NG; i++) yv[i] = reinterpret_cast<const f32x4*>(Y + (size_t)max(pv[i], 0) * H)[c4];
+#pragma unroll
+        for (int i = 0; i < NG; i++) {
+            const int j = j0 + i;
+            if (j >= k) break;
+            const float wj = wv[i];
+            if (pv[i] < 0) {
+                acc = f32x4{__uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u), __uint_as_float(0x7FC00000u),
+                            __uint_as_float(0x7FC00000u)};
+                continue;
+            }
+            acc.x = fmaf(wj, yv[i].x, acc.x);
+            acc.y = fmaf(wj, yv[i].y, acc.y);
+            acc.z = fmaf(wj, yv[i].z, acc.z);
+            acc.w = fmaf(wj, yv[i].w, acc.w);
+        }
     }
     if (out_bf16) {
         const f32x2 p0 = {acc.x, acc.y}, p1 = {acc.z, acc.w};
