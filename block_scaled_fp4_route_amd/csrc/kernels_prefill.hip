@@ -543,7 +543,9 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 
 // Shared K loop of the two NVFP4 GEMMs: acc[rb][cb] += A[16 RB rows] x B[4
 // column blocks]^T over K (= KTOT) in chunks of BK (128 or 256), the A tile
-// staged in LDS as MR rows (64 or 128; RB <= MR/16) per chunk. A is a
+// staged in LDS as MR rows (16, 32, 64 or 128; RB <= MR/16) per chunk: a tile
+// of 1 or 2 row blocks loads only those rows (each A load instruction
+// writes LDS even where its rows are past the tile's end). A is a
 // buffer of a_bytes bytes; a_row(r) gives the element offset of A row r
 // (0 <= r < rows). blk is the expert block (block_bytes), codes_off and
 // scl_off the byte offsets of the weight matrix's code and scale regions
@@ -586,6 +588,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
                                          __bf16* lds, const uint8_t* slds, int srow0) {
     constexpr int SPR = BK / 8;       // 16-byte pieces per A row
     constexpr int NAI = MR * SPR / 256;  // A loads per wave per chunk (MR rows x SPR pieces over 256 lanes)
+    static_assert(NAI >= 1 && NAI * 256 == MR * SPR && RB * 16 <= MR, "A tile shape");
     constexpr int QK = BK / 4;        // K per lane group
     constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
     constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
@@ -667,8 +670,8 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
             const __bf16* At = lds + (size_t)(ch & 1) * MR * BK;
 #pragma unroll
             for (int s = 0; s < NS; s++) {
-                // the A fragments of all row blocks first (the MR-row tile is
-                // always allocated), so their LDS latency hides behind the decode
+                // the A fragments of all row blocks first, so their LDS
+                // latency hides behind the decode
                 const int p = (QK / 8) * g + s;  // 16-byte piece of the fragment
                 // fragments as 16-byte vectors of the operand type
                 typedef std::conditional_t<F16, f16x8, bf16x8> opv;
@@ -784,9 +787,9 @@ __global__ __launch_bounds__(256, 2) void k_gateup_nv(GemmArgs a) {
     // the K loop is specialised on the tile's row blocks (wave-uniform); a
     // 128-row tile takes 128-wide K chunks so that its A tile fits the same LDS
     if (rows <= 16)
-        gateup_nv_tile<1, kBKGate, 64>(a, lds, e, base, rows, nt);
+        gateup_nv_tile<1, kBKGate, 16>(a, lds, e, base, rows, nt);
     else if (rows <= 32)
-        gateup_nv_tile<2, kBKGate, 64>(a, lds, e, base, rows, nt);
+        gateup_nv_tile<2, kBKGate, 32>(a, lds, e, base, rows, nt);
     else if (rows <= 64)
         gateup_nv_tile<4, kBKGate, 64>(a, lds, e, base, rows, nt);
     else
@@ -856,9 +859,9 @@ __global__ __launch_bounds__(256, 2) void k_down_nv(GemmArgs a) {
         }
     }
     if (rows <= 16)
-        down_nv_tile<1, 64, SL>(a, lds, sl, e, base, rows, nt);
+        down_nv_tile<1, 16, SL>(a, lds, sl, e, base, rows, nt);
     else if (rows <= 32)
-        down_nv_tile<2, 64, SL>(a, lds, sl, e, base, rows, nt);
+        down_nv_tile<2, 32, SL>(a, lds, sl, e, base, rows, nt);
     else if (rows <= 64)
         down_nv_tile<4, 64, SL>(a, lds, sl, e, base, rows, nt);
     else
