@@ -790,6 +790,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_nv(GemmArgs a) {
         gateup_nv_tile<1, kBKGate, 16>(a, lds, e, base, rows, nt);
     else if (rows <= 32)
         gateup_nv_tile<2, kBKGate, 32>(a, lds, e, base, rows, nt);
+    else if (rows <= 48)
+        gateup_nv_tile<3, kBKGate, 48>(a, lds, e, base, rows, nt);
     else if (rows <= 64)
         gateup_nv_tile<4, kBKGate, 64>(a, lds, e, base, rows, nt);
     else
@@ -862,6 +864,8 @@ __global__ __launch_bounds__(256, 2) void k_down_nv(GemmArgs a) {
         down_nv_tile<1, 16, SL>(a, lds, sl, e, base, rows, nt);
     else if (rows <= 32)
         down_nv_tile<2, 32, SL>(a, lds, sl, e, base, rows, nt);
+    else if (rows <= 48)
+        down_nv_tile<3, 48, SL>(a, lds, sl, e, base, rows, nt);
     else if (rows <= 64)
         down_nv_tile<4, 64, SL>(a, lds, sl, e, base, rows, nt);
     else
