@@ -3,12 +3,13 @@
 // the whole prompt through each layer, so each expert's weights are read
 // once per prompt instead of once per chunk).
 //
-//  1. k_group: stable grouping of the T*k assignments a = t*k + j by expert
-//     (count, exclusive prefix sum, ordered compaction with ballots:
-//     deterministic, no atomics).
+//  1. grouping (k_front): stable grouping of the T*k assignments a = t*k + j
+//     by expert (count, exclusive prefix sum, ordered compaction with
+//     ballots: deterministic, no atomics).
 //  2. k_tile_list: M-tiles of every expert, heaviest experts first.
-//  3. k_quant_*: x~ = bf16(x) (NVFP4 layers; held for the GEMM as fp16 times
-//     a power of two per token, exactly) or MXFP4 per 32 (MXFP4 layers).
+//  3. activation rounding (k_front, beside the grouping; k_quant_mx for h):
+//     x~ = bf16(x) (NVFP4 layers; held for the GEMM as fp16 times a power of
+//     two per token, exactly) or MXFP4 per 32 (MXFP4 layers).
 //  4. ragged grouped GEMMs (gate/up with SiLU*mul epilogue, then down):
 //     NVFP4 weights are decoded in registers, exactly, to fp16 for gate/up
 //     (v_mfma_f32_16x16x32_f16) and to bf16 for down against h~
@@ -118,7 +119,7 @@ __device__ __forceinline__ int wave_sum_int(int v) {
     return v;
 }
 
-// grid ceil(E/4), 1024 threads; workgroup b handles the experts e0 = 4b ..
+// G = ceil(E/4) workgroups of 1024 threads; workgroup b handles the experts e0 = 4b ..
 // e0+3 (those below E) and no workgroup depends on another. Wave w owns the
 // contiguous slice [n*w/16, n*(w+1)/16) of the assignments a = t*k + j; its
 // lane l takes a = lo + 64*i + l, so the order (i, l) is increasing a. Each
@@ -136,13 +137,13 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 constexpr int kGroupPer = 24;
 constexpr int kGroupExperts = 4;
 
-__global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ idx, int n, int E,
-                                                         int* __restrict__ count, int* __restrict__ off,
-                                                         int* __restrict__ perm, int* __restrict__ pos) {
+__device__ __forceinline__ void group_block(const int32_t* __restrict__ idx, int n, int E, int* __restrict__ count,
+                                            int* __restrict__ off, int* __restrict__ perm, int* __restrict__ pos,
+                                            int bid, int G) {
     constexpr int NW = kGroupThreads / 64, ND = kGroupExperts;
     __shared__ int red_lt[NW], red_eq[ND][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e0 = ND * blockIdx.x;
+    const int e0 = ND * bid;
     const int lo = (int)((long long)n * wave / NW), hi = (int)((long long)n * (wave + 1) / NW);
     int lt = 0, eq[ND] = {};
     for (int a0 = lo; a0 < hi; a0 += 64 * kGroupPer) {
@@ -187,8 +188,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restri
         }
         base += cnt;
     }
-    const int G = gridDim.x;
-    const int slo = (int)((long long)n * blockIdx.x / G), shi = (int)((long long)n * (blockIdx.x + 1) / G);
+    const int slo = (int)((long long)n * bid / G), shi = (int)((long long)n * (bid + 1) / G);
     for (int a = slo + tid; a < shi; a += kGroupThreads)
         if ((unsigned)idx[a] >= (unsigned)E) pos[a] = -1;
     if (mine == 0) return;  // wave-uniform: this wave's slice holds no match
@@ -339,9 +339,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
 // One wave per row, the row read twice (the second pass from L2) in blocks
 // of 16 float4 per lane whose loads are all issued before the first use.
 constexpr int kQuantBlk = 16;
-__global__ __launch_bounds__(256) void k_quant_f16(const float* __restrict__ x, int T, int H, f16x2* __restrict__ out,
-                                                   int* __restrict__ xexp, bf16x2* __restrict__ xdbg) {
-    const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + wave_id(), H4 = H / 4;
+__device__ __forceinline__ void quant_f16_row(const float* __restrict__ x, int T, int H, f16x2* __restrict__ out,
+                                              int* __restrict__ xexp, bf16x2* __restrict__ xdbg, int row) {
+    const int lane = threadIdx.x & 63, H4 = H / 4;
     if (row >= T) return;
     const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)row * H);
     auto to_bf16 = [](const f32x4 a, bf16x2& q0, bf16x2& q1) {
@@ -405,10 +405,9 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
 // clamped to [-127, 127]; scale byte X + 127 (0 for an all-zero block);
 // codes e2m1(|v| / 2^X) with the sign of v. Codes packed two per byte, the
 // even element in the low nibble.
-__global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src, size_t nblocks,
-                                                  uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                  float* __restrict__ dequant) {
-    const size_t b = (size_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void quant_mx_block(const float* __restrict__ src, size_t nblocks,
+                                               uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                               float* __restrict__ dequant, size_t b) {
     if (b >= nblocks) return;
     const f32x4* p = reinterpret_cast<const f32x4*>(src + b * 32);
     float v[32];
@@ -446,6 +445,47 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
             q[0] = d0.x * s; q[1] = d0.y * s; q[2] = d1.x * s; q[3] = d1.y * s;
             q[4] = d2.x * s; q[5] = d2.y * s; q[6] = d3.x * s; q[7] = d3.y * s;
         }
+    }
+}
+
+// The rounding of h (MXFP4 layers) between the two GEMMs: one thread per
+// block of 32.
+__global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src, size_t nblocks,
+                                                  uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  float* __restrict__ dequant) {
+    quant_mx_block(src, nblocks, codes, scales, dequant, (size_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// The first launch of a prefill call: grouping and the rounding of x, which
+// share no data, side by side. Workgroups 0 .. G-1 (G = ceil(E/4)) group the
+// assignments (group_block); the workgroups after them round x: 16 rows
+// each, one per wave (NVFP4), or 1024 MX blocks, one per thread (MXFP4).
+struct FrontArgs {
+    const int32_t* idx;
+    int n, E, G;
+    int* count;
+    int* off;
+    int* perm;
+    int* pos;
+    const float* x;
+    int T, H;
+    f16x2* xq;         // NVFP4: fp16 x~ [T][H]
+    int* xexp;         // NVFP4: [T]
+    bf16x2* xdbg;      // NVFP4: bf16 x~ (debug) or null
+    uint32_t* xcodes;  // MXFP4: codes [T][H/2]
+    uint8_t* xscales;  // MXFP4: scales [T][H/32]
+    size_t nbx;        // MXFP4: blocks of 32 in x
+};
+
+template <bool NV>
+__global__ __launch_bounds__(kGroupThreads) void k_front(FrontArgs f) {
+    const int b = (int)blockIdx.x;
+    if (b < f.G) {
+        group_block(f.idx, f.n, f.E, f.count, f.off, f.perm, f.pos, b, f.G);
+    } else if constexpr (NV) {
+        quant_f16_row(f.x, f.T, f.H, f.xq, f.xexp, f.xdbg, (b - f.G) * (kGroupThreads / 64) + wave_id());
+    } else {
+        quant_mx_block(f.x, f.nbx, f.xcodes, f.xscales, nullptr, (size_t)(b - f.G) * kGroupThreads + threadIdx.x);
     }
 }
 
@@ -1232,7 +1272,22 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     int* perm = dbg && dbg->perm ? dbg->perm : L.perm;
     int* off = dbg && dbg->off ? dbg->off : L.off;
 
-    hipLaunchKernelGGL(k_group, dim3((E + kGroupExperts - 1) / kGroupExperts), dim3(kGroupThreads), 0, s, idx, n, E, L.count, off, perm, L.pos);
+    FrontArgs fa = {};
+    fa.idx = idx; fa.n = n; fa.E = E; fa.G = (E + kGroupExperts - 1) / kGroupExperts;
+    fa.count = L.count; fa.off = off; fa.perm = perm; fa.pos = L.pos;
+    fa.x = x; fa.T = T; fa.H = H;
+    uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);
+    uint8_t* xs = dbg && dbg->x_scales ? dbg->x_scales : reinterpret_cast<uint8_t*>(L.xq) + (size_t)T * H / 2;
+    if (fmt == kFmtNvfp4) {
+        fa.xq = reinterpret_cast<f16x2*>(L.xq); fa.xexp = L.xexp;
+        fa.xdbg = dbg && dbg->x_bf16 ? reinterpret_cast<bf16x2*>(dbg->x_bf16) : (bf16x2*)nullptr;
+        const int nq = (T + kGroupThreads / 64 - 1) / (kGroupThreads / 64);
+        hipLaunchKernelGGL(k_front<true>, dim3((unsigned)(fa.G + nq)), dim3(kGroupThreads), 0, s, fa);
+    } else {
+        fa.xcodes = reinterpret_cast<uint32_t*>(xc); fa.xscales = xs; fa.nbx = (size_t)T * H / 32;
+        const int nq = (int)((fa.nbx + kGroupThreads - 1) / kGroupThreads);
+        hipLaunchKernelGGL(k_front<false>, dim3((unsigned)(fa.G + nq)), dim3(kGroupThreads), 0, s, fa);
+    }
     LAUNCH_CHECK();
     TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
     hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, fmt == kFmtNvfp4 ? kBM_NV2 : 0, kNV2Min, L.tile_e, L.tile_m, L.ntiles,
@@ -1245,9 +1300,6 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     ga.h_pre = dbg ? dbg->h_pre : nullptr;
 
     if (fmt == kFmtNvfp4) {
-        hipLaunchKernelGGL(k_quant_f16, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, reinterpret_cast<f16x2*>(L.xq), L.xexp,
-                           dbg && dbg->x_bf16 ? reinterpret_cast<bf16x2*>(dbg->x_bf16) : (bf16x2*)nullptr);
-        LAUNCH_CHECK();
         ga.a_src = L.xq;
         ga.xexp = L.xexp; ga.out = L.hq; ga.h_q = dbg ? dbg->h_q : nullptr; ga.NT = I / 128;
         ga.a_bytes = (uint32_t)((size_t)T * H * 2);
@@ -1263,12 +1315,6 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
             hipLaunchKernelGGL(k_down_nv<false>, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
         LAUNCH_CHECK();
     } else {
-        uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);
-        uint8_t* xs = dbg && dbg->x_scales ? dbg->x_scales : reinterpret_cast<uint8_t*>(L.xq) + (size_t)T * H / 2;
-        const size_t nbx = (size_t)T * H / 32;
-        hipLaunchKernelGGL(k_quant_mx, dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s, x, nbx,
-                           reinterpret_cast<uint32_t*>(xc), xs, (float*)nullptr);
-        LAUNCH_CHECK();
         ga.a_src = xc; ga.a_scl = xs; ga.out = L.hf;
         ga.a_bytes = (uint32_t)((size_t)T * H / 2);
         ga.a_scl_bytes = (uint32_t)((size_t)T * H / 32);
