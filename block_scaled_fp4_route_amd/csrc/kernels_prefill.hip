@@ -6,7 +6,8 @@
 //  1. grouping (k_front): stable grouping of the T*k assignments a = t*k + j
 //     by expert (count, exclusive prefix sum, ordered compaction with
 //     ballots: deterministic, no atomics).
-//  2. k_tile_list: M-tiles of every expert, heaviest experts first.
+//  2. tile list (k_front, beside the grouping): M-tiles of every expert,
+//     heaviest experts first.
 //  3. activation rounding (k_front, beside the grouping; k_quant_mx for h):
 //     x~ = bf16(x) (NVFP4 layers; held for the GEMM as fp16 times a power of
 //     two per token, exactly) or MXFP4 per 32 (MXFP4 layers).
@@ -221,7 +222,9 @@ __device__ __forceinline__ void group_block(const int32_t* __restrict__ idx, int
 // ---------------------------------------------------------------------------
 // 2. tile list: experts ordered by row count (descending; ties by index),
 // each split into M-tiles of BM rows, or of BM2 rows if it has at least
-// BM2min (BM2 = 0: one height).
+// BM2min (BM2 = 0: one height). One workgroup of 1024 threads, which counts
+// the rows of every expert itself (an LDS histogram of idx), so that it
+// depends on nothing but the routing and runs beside the grouping.
 //
 // With rec != nullptr it also writes one record per slot of the max_tiles
 // slots: the expert block, the first grouped row and the row count of the
@@ -234,12 +237,13 @@ struct TileRec {
 };
 static_assert(sizeof(TileRec) == 16, "tile record is 16 bytes");
 
-__global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restrict__ count, int E, int BM, int BM2, int BM2min,
-                                                             int* __restrict__ tile_e, int* __restrict__ tile_m,
-                                                             int* __restrict__ ntiles, TileRec* __restrict__ rec,
-                                                             int max_slots, const int* __restrict__ off,
-                                                             const void* const* __restrict__ expert_ptrs) {
+__device__ __forceinline__ void tile_list_block(const int32_t* __restrict__ idx, int n, int E, int BM, int BM2,
+                                                int BM2min, int* __restrict__ tile_e, int* __restrict__ tile_m,
+                                                int* __restrict__ ntiles, TileRec* __restrict__ rec, int max_slots,
+                                                const void* const* __restrict__ expert_ptrs) {
+    static_assert(kMaxE <= kGroupThreads, "one thread per expert in the scans");
     __shared__ int cnt[kMaxE];
+    __shared__ int offs[kMaxE];
     __shared__ uint4 key4[kMaxE / 4];
     __shared__ int rank[kMaxE];
     __shared__ int nt_sorted[kMaxE];
@@ -248,13 +252,43 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
     unsigned* key = reinterpret_cast<unsigned*>(key4);
     const int tid = threadIdx.x;
     const int E4 = (E + 3) / 4;
+    // rows per expert (assignments with an index outside [0, E) count nowhere)
+    for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int a0 = 0; a0 < n; a0 += kGroupThreads * kGroupPer) {
+        int v[kGroupPer];
+#pragma unroll
+        for (int i = 0; i < kGroupPer; i++) {
+            const int a = a0 + kGroupThreads * i + tid;
+            v[i] = a < n ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kGroupPer; i++)
+            if ((unsigned)v[i] < (unsigned)E) atomicAdd(&cnt[v[i]], 1);
+    }
+    __syncthreads();
+    // inclusive scan over threads (Hillis-Steele; kGroupThreads >= E entries)
+    auto scan = [&](int v) {
+        for (int d = 1; d < kGroupThreads; d <<= 1) {
+            start[tid] = v;
+            __syncthreads();
+            if (tid >= d) v += start[tid - d];
+            __syncthreads();
+        }
+        return v;
+    };
+    if (rec) {
+        // first grouped row of every expert (the grouping's exclusive prefix sum)
+        const int c = tid < E ? cnt[tid] : 0;
+        const int inc = scan(c);
+        if (tid < E) offs[tid] = inc - c;
+    }
     // key: larger count first, then lower index (counts clamped to 22 bits,
     // which only coarsens the order of the tile list)
     for (int e = tid; e < 4 * E4; e += kGroupThreads) {
         int c = 0;
         if (e < E) {
-            c = count[e];
-            cnt[e] = c;
+            c = cnt[e];
             rank[e] = 0;
         }
         key[e] = e < E ? ((0x3FFFFFu - (unsigned)min(c, 0x3FFFFF)) << 10) | (unsigned)e : 0xFFFFFFFFu;
@@ -281,14 +315,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
         nt_sorted[rank[e]] = (cnt[e] + height(cnt[e]) - 1) / height(cnt[e]);
     }
     __syncthreads();
-    // inclusive scan of nt_sorted (Hillis-Steele over kGroupThreads >= E entries)
-    int v = tid < E ? nt_sorted[tid] : 0;
-    for (int d = 1; d < kGroupThreads; d <<= 1) {
-        start[tid] = v;
-        __syncthreads();
-        if (tid >= d) v += start[tid - d];
-        __syncthreads();
-    }
+    // inclusive scan of nt_sorted
+    const int v = scan(tid < E ? nt_sorted[tid] : 0);
     start[tid + 1] = v;          // start[r + 1] = tiles of ranks 0..r
     if (tid == 0) start[0] = 0;
     if (tid == kGroupThreads - 1) ntiles[0] = v;
@@ -316,7 +344,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_tile_list(const int* __restri
         if (rec) {
             TileRec t;
             t.blk = reinterpret_cast<const uint8_t*>(expert_ptrs[e]);
-            t.base = off[e] + m * bm;
+            t.base = offs[e] + m * bm;
             t.rows = min(bm, cnt[e] - m * bm);
             rec[sl] = t;
         }
@@ -456,10 +484,12 @@ __global__ __launch_bounds__(256) void k_quant_mx(const float* __restrict__ src,
     quant_mx_block(src, nblocks, codes, scales, dequant, (size_t)blockIdx.x * 256 + threadIdx.x);
 }
 
-// The first launch of a prefill call: grouping and the rounding of x, which
-// share no data, side by side. Workgroups 0 .. G-1 (G = ceil(E/4)) group the
-// assignments (group_block); the workgroups after them round x: 16 rows
-// each, one per wave (NVFP4), or 1024 MX blocks, one per thread (MXFP4).
+// The first launch of a prefill call: the tile list, the grouping and the
+// rounding of x, which depend only on the routing and x, side by side.
+// Workgroup 0 builds the tile list (tile_list_block, first: the GEMMs wait on
+// it longest); workgroups 1 .. G (G = ceil(E/4)) group the assignments
+// (group_block); the workgroups after them round x: 16 rows each, one per
+// wave (NVFP4), or 1024 MX blocks, one per thread (MXFP4).
 struct FrontArgs {
     const int32_t* idx;
     int n, E, G;
@@ -475,12 +505,22 @@ struct FrontArgs {
     uint32_t* xcodes;  // MXFP4: codes [T][H/2]
     uint8_t* xscales;  // MXFP4: scales [T][H/32]
     size_t nbx;        // MXFP4: blocks of 32 in x
+    int BM, BM2, BM2min;  // tile heights (tile_list_block)
+    int* tile_e;
+    int* tile_m;
+    int* ntiles;
+    TileRec* rec;
+    int max_slots;
+    const void* const* expert_ptrs;
 };
 
 template <bool NV>
 __global__ __launch_bounds__(kGroupThreads) void k_front(FrontArgs f) {
-    const int b = (int)blockIdx.x;
-    if (b < f.G) {
+    const int b = (int)blockIdx.x - 1;
+    if (b < 0) {
+        tile_list_block(f.idx, f.n, f.E, f.BM, f.BM2, f.BM2min, f.tile_e, f.tile_m, f.ntiles, f.rec, f.max_slots,
+                        f.expert_ptrs);
+    } else if (b < f.G) {
         group_block(f.idx, f.n, f.E, f.count, f.off, f.perm, f.pos, b, f.G);
     } else if constexpr (NV) {
         quant_f16_row(f.x, f.T, f.H, f.xq, f.xexp, f.xdbg, (b - f.G) * (kGroupThreads / 64) + wave_id());
@@ -1276,22 +1316,22 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     fa.idx = idx; fa.n = n; fa.E = E; fa.G = (E + kGroupExperts - 1) / kGroupExperts;
     fa.count = L.count; fa.off = off; fa.perm = perm; fa.pos = L.pos;
     fa.x = x; fa.T = T; fa.H = H;
+    TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
+    fa.BM = BM; fa.BM2 = fmt == kFmtNvfp4 ? kBM_NV2 : 0; fa.BM2min = kNV2Min;
+    fa.tile_e = L.tile_e; fa.tile_m = L.tile_m; fa.ntiles = L.ntiles; fa.rec = rec; fa.max_slots = mt;
+    fa.expert_ptrs = expert_ptrs;
     uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);
     uint8_t* xs = dbg && dbg->x_scales ? dbg->x_scales : reinterpret_cast<uint8_t*>(L.xq) + (size_t)T * H / 2;
     if (fmt == kFmtNvfp4) {
         fa.xq = reinterpret_cast<f16x2*>(L.xq); fa.xexp = L.xexp;
         fa.xdbg = dbg && dbg->x_bf16 ? reinterpret_cast<bf16x2*>(dbg->x_bf16) : (bf16x2*)nullptr;
         const int nq = (T + kGroupThreads / 64 - 1) / (kGroupThreads / 64);
-        hipLaunchKernelGGL(k_front<true>, dim3((unsigned)(fa.G + nq)), dim3(kGroupThreads), 0, s, fa);
+        hipLaunchKernelGGL(k_front<true>, dim3((unsigned)(1 + fa.G + nq)), dim3(kGroupThreads), 0, s, fa);
     } else {
         fa.xcodes = reinterpret_cast<uint32_t*>(xc); fa.xscales = xs; fa.nbx = (size_t)T * H / 32;
         const int nq = (int)((fa.nbx + kGroupThreads - 1) / kGroupThreads);
-        hipLaunchKernelGGL(k_front<false>, dim3((unsigned)(fa.G + nq)), dim3(kGroupThreads), 0, s, fa);
+        hipLaunchKernelGGL(k_front<false>, dim3((unsigned)(1 + fa.G + nq)), dim3(kGroupThreads), 0, s, fa);
     }
-    LAUNCH_CHECK();
-    TileRec* rec = fmt == kFmtMxfp4 ? reinterpret_cast<TileRec*>(L.rec) : nullptr;
-    hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(kGroupThreads), 0, s, L.count, E, BM, fmt == kFmtNvfp4 ? kBM_NV2 : 0, kNV2Min, L.tile_e, L.tile_m, L.ntiles,
-                       rec, mt, off, expert_ptrs);
     LAUNCH_CHECK();
 
     GemmArgs ga = {};
