@@ -512,12 +512,15 @@ struct FrontArgs {
     TileRec* rec;
     int max_slots;
     const void* const* expert_ptrs;
+    int* done;         // NVFP4: the GEMM launch's tile counters (4 ints per tile slot), cleared here
 };
 
 template <bool NV>
 __global__ __launch_bounds__(kGroupThreads) void k_front(FrontArgs f) {
     const int b = (int)blockIdx.x - 1;
     if (b < 0) {
+        if (f.done)
+            for (int i = threadIdx.x; i < 4 * f.max_slots; i += kGroupThreads) f.done[i] = 0;
         tile_list_block(f.idx, f.n, f.E, f.BM, f.BM2, f.BM2min, f.tile_e, f.tile_m, f.ntiles, f.rec, f.max_slots,
                         f.expert_ptrs);
     } else if (b < f.G) {
@@ -548,19 +551,25 @@ __global__ __launch_bounds__(kGroupThreads) void k_front(FrontArgs f) {
 // two instructions per two codes (conversion, packed multiply) where bf16
 // takes four, since the hardware conversion applies only the exponent of a
 // scale and gfx950 has no packed bf16 multiply. x~ comes as fp16 times 2^t
-// per token (k_quant_f16), and the epilogue multiplies the sums by 2^-t.
+// per token (the front launch), and the epilogue multiplies the sums by 2^-t.
 // Workgroup -> (M-tile, N-tile). Workgroups are dispatched round-robin over
 // the 8 XCDs (each with its own L2), so workgroup b runs on XCD b % 8. M-tile
 // t goes to XCD t % 8 and all NT N-tiles of an M-tile (the same gathered
 // activation rows) to that XCD, one after the other: the tile list is sorted
 // heaviest expert first, so dealing M-tiles round-robin spreads the full
 // tiles evenly over the XCDs. The grid is 8 * ceil(max_tiles / 8) * NT.
-// Returns false for workgroups beyond the real tiles.
-__device__ __forceinline__ bool map_tile(int ntiles, int NT, int& tile, int& nt) {
-    const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+// bid: the workgroup's index within its part of the launch (the down part
+// of the GEMM launch starts at a multiple of 8, so a tile's gate/up and down
+// workgroups share an XCD). Returns false for workgroups beyond the real
+// tiles.
+__device__ __forceinline__ bool map_tile_b(int bid, int ntiles, int NT, int& tile, int& nt) {
+    const int x = bid % 8, j = bid / 8;
     tile = x + 8 * (j / NT);
     nt = j % NT;
     return tile < ntiles;
+}
+__device__ __forceinline__ bool map_tile(int ntiles, int NT, int& tile, int& nt) {
+    return map_tile_b((int)blockIdx.x, ntiles, NT, tile, nt);
 }
 
 struct GemmArgs {
@@ -856,11 +865,12 @@ __device__ __forceinline__ int nv_tile_rows(const GemmArgs& a, int e, int m0) {
     return min(c >= kNV2Min ? kBM_NV2 : kBM_NV, c - m0);
 }
 
-__global__ __launch_bounds__(256, 2) void k_gateup_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * 64 * kBKGate];  // = 2 * kBM_NV2 * 128
+// The gate/up part of workgroup bid of the GEMM launch (lds: 2 * 64 *
+// kBKGate bf16); returns its tile, or -1 if it has none.
+__device__ __forceinline__ int gateup_part(const GemmArgs& a, __bf16* lds, int bid) {
     static_assert(2 * 64 * kBKGate == 2 * kBM_NV2 * 128, "one LDS size for both tile heights");
     int tile, nt;
-    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
+    if (!map_tile_b(bid, a.ntiles[0], a.NT, tile, nt)) return -1;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = nv_tile_rows(a, e, m0);
     const int base = a.off[e] + m0;
@@ -876,6 +886,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_nv(GemmArgs a) {
         gateup_nv_tile<4, kBKGate, 64>(a, lds, e, base, rows, nt);
     else
         gateup_nv_tile<8, 128, kBM_NV2>(a, lds, e, base, rows, nt);
+    return tile;
 }
 
 // 4b. NVFP4 down: Y[p][n] = sum_i h~[p][i] * Wd[n][i]. Workgroup = (M-tile of
@@ -919,15 +930,44 @@ __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, con
             }
 }
 
+// Bound of the down part's wait for its tile's h~, in polls of ~256 cycles
+// (~0.4 s): a wait that ends unmet poisons the tile's outputs with NaN.
+constexpr int kTileWaitPolls = 1 << 22;
+
+// The down part of workgroup bid of the GEMM launch (lds: 2 * kBM_NV2 *
+// kBKDown bf16; sl: 256 * kDownSclMaxI / 16 bytes). It first waits until
+// done[4 * tile] reaches `need`, the count of the tile's gate/up workgroups.
 template <bool SL>
-__global__ __launch_bounds__(256, 2) void k_down_nv(GemmArgs a) {
-    __shared__ __bf16 lds[2 * kBM_NV2 * kBKDown];
-    __shared__ __attribute__((aligned(16))) uint8_t sl[SL ? 256 * kDownSclMaxI / 16 : 16];
+__device__ __forceinline__ void down_part(const GemmArgs& a, __bf16* lds, uint8_t* sl, int bid, const int* done,
+                                          int need) {
     int tile, nt;
-    if (!map_tile(a.ntiles[0], a.NT, tile, nt)) return;
+    if (!map_tile_b(bid, a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
     const int rows = nv_tile_rows(a, e, m0);
     const int base = a.off[e] + m0;
+    // the outcome of thread 0's wait goes to every thread through the first
+    // LDS word (no extra LDS: the second barrier keeps the A tiles from
+    // overwriting it before every thread has read it)
+    int* flag = reinterpret_cast<int*>(lds);
+    if (threadIdx.x == 0) {
+        int c = 0, polls = 0;
+        while ((c = __hip_atomic_load(done + 4 * tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need &&
+               ++polls < kTileWaitPolls)
+            __builtin_amdgcn_s_sleep(4);
+        *flag = c >= need;
+    }
+    __syncthreads();
+    const bool ready = *flag != 0;
+    __syncthreads();
+    // h~ was written on this XCD (same L2, see k_gemms_nv); no stale line of
+    // it may remain in this compute unit's L1
+    asm volatile("buffer_inv sc0" ::: "memory");
+    if (!ready) {
+        float* Y = reinterpret_cast<float*>(a.out);
+        for (int i = threadIdx.x; i < rows * 256; i += 256)
+            Y[(size_t)(base + i / 256) * a.H + nt * 256 + i % 256] = __uint_as_float(0x7FC00000u);
+        return;
+    }
     if constexpr (SL) {
         // 1 KB loads of the rows' scales; they are older than the K loop's
         // first loads, so its first wait covers them
@@ -952,8 +992,45 @@ __global__ __launch_bounds__(256, 2) void k_down_nv(GemmArgs a) {
         down_nv_tile<8, kBM_NV2, SL>(a, lds, sl, e, base, rows, nt);
 }
 
+// 4c. The two NVFP4 GEMMs in one launch. Workgroups 0 .. ngu-1 run gate/up
+// (k_gateup's tiles), workgroups ngu .. the down GEMM of the same tiles; ngu
+// is a multiple of 8. Down workgroup (tile t, N-tile) starts only once the
+// NT gate/up workgroups of tile t have published its h~ rows: each of those
+// waits until its own stores have reached L2, then adds 1 to done[4t] (an
+// atomic in L2); the down workgroup polls that counter (bounded) and
+// invalidates its L1 before loading h~. No L2 write-back or invalidation is
+// needed: with workgroup b on XCD b % 8 (the dispatcher deals workgroups
+// round-robin over the XCDs; with 1, 2 or 4 XCDs the same congruence holds),
+// a tile's gate/up and down workgroups have equal indices mod 8 and share
+// one L2, and every h~ element is written once per call. The dispatcher
+// starts workgroups in index order, so every gate/up workgroup has started
+// before the first down workgroup waits: the waits end. The down work of
+// the heavy tiles (first in the list) then fills the gate/up tail. done[] is
+// cleared by the front launch.
+struct GemmPair {
+    GemmArgs gu, dn;
+    int ngu;
+    int* done;
+};
+template <bool SL>
+__global__ __launch_bounds__(256, 2) void k_gemms_nv(GemmPair f) {
+    // gate/up: 64 KB of A tiles; down: 64 KB of A tiles + the staged scales
+    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kBM_NV2 * kBKDown + 256 * kDownSclMaxI / 16 / 2];
+    static_assert(2 * 64 * kBKGate == 2 * kBM_NV2 * kBKDown, "one A-tile LDS size for both GEMMs");
+    const int b = (int)blockIdx.x;
+    if (b < f.ngu) {
+        const int tile = gateup_part(f.gu, lds, b);
+        if (tile < 0) return;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's h~ stores have reached L2
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(f.done + 4 * tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        down_part<SL>(f.dn, lds, reinterpret_cast<uint8_t*>(lds + 2 * kBM_NV2 * kBKDown), b - f.ngu, f.done, f.gu.NT);
+    }
+}
+
 // ---------------------------------------------------------------------------
-// 4c. MXFP4 grouped GEMMs: v_mfma_scale_f32_16x16x128_f8f6f4 on the e2m1
+// 4d. MXFP4 grouped GEMMs: v_mfma_scale_f32_16x16x128_f8f6f4 on the e2m1
 // codes of both operands with their UE8M0 block scales (a design choice of
 // this library: the FP4 weights go to the matrix cores as stored, never
 // widened). With a few tokens per expert these GEMMs stream the expert
@@ -1320,6 +1397,7 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
     fa.BM = BM; fa.BM2 = fmt == kFmtNvfp4 ? kBM_NV2 : 0; fa.BM2min = kNV2Min;
     fa.tile_e = L.tile_e; fa.tile_m = L.tile_m; fa.ntiles = L.ntiles; fa.rec = rec; fa.max_slots = mt;
     fa.expert_ptrs = expert_ptrs;
+    fa.done = fmt == kFmtNvfp4 ? reinterpret_cast<int*>(L.rec) : nullptr;
     uint8_t* xc = dbg && dbg->x_codes ? dbg->x_codes : reinterpret_cast<uint8_t*>(L.xq);
     uint8_t* xs = dbg && dbg->x_scales ? dbg->x_scales : reinterpret_cast<uint8_t*>(L.xq) + (size_t)T * H / 2;
     if (fmt == kFmtNvfp4) {
@@ -1344,15 +1422,16 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         ga.xexp = L.xexp; ga.out = L.hq; ga.h_q = dbg ? dbg->h_q : nullptr; ga.NT = I / 128;
         ga.a_bytes = (uint32_t)((size_t)T * H * 2);
         ga.block_bytes = (uint32_t)((size_t)3 * H * I / 2 + (size_t)3 * H * I / 16);
-        hipLaunchKernelGGL(k_gateup_nv, dim3(gemm_grid(mt, ga.NT)), dim3(256), 0, s, ga);
-        LAUNCH_CHECK();
         GemmArgs gd = ga;
         gd.a_src = L.hq; gd.out = L.Y; gd.h_pre = nullptr; gd.h_q = nullptr; gd.NT = H / 256;
         gd.a_bytes = (uint32_t)((size_t)n * I * 2);
+        GemmPair gp;
+        gp.gu = ga; gp.dn = gd; gp.ngu = (int)gemm_grid(mt, ga.NT); gp.done = reinterpret_cast<int*>(L.rec);
+        const dim3 grid((unsigned)gp.ngu + gemm_grid(mt, gd.NT));
         if (I <= kDownSclMaxI)
-            hipLaunchKernelGGL(k_down_nv<true>, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+            hipLaunchKernelGGL(k_gemms_nv<true>, grid, dim3(256), 0, s, gp);
         else
-            hipLaunchKernelGGL(k_down_nv<false>, dim3(gemm_grid(mt, gd.NT)), dim3(256), 0, s, gd);
+            hipLaunchKernelGGL(k_gemms_nv<false>, grid, dim3(256), 0, s, gp);
         LAUNCH_CHECK();
     } else {
         ga.a_src = xc; ga.a_scl = xs; ga.out = L.hf;
