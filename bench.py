@@ -45,8 +45,8 @@ TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
     "qwen_decode": (38256128, "59e88a0decc5560a"),
     "qwen_layer_decode": (28344013, "59e88a0decc5560a"),
     "deepseek_decode": (114379776, "59e88a0decc5560a"),
-    "qwen_prefill": (2748197683, "1d4ae9079e29c0e3"),
-    "deepseek_prefill": (7298329805, "1d4ae9079e29c0e3"),
+    "qwen_prefill": (2692465664, "0dd5e43931fef604"),
+    "deepseek_prefill": (7298339226, "0dd5e43931fef604"),
     "fp8_act_quant": (21128192, "3e24836c4e0819a4"),
     "fp8_gemv": (21209088, "3e24836c4e0819a4"),
 }
