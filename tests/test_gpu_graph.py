@@ -185,3 +185,41 @@ def test_fp8_kernels_in_a_graph(m, orc):
     oc, osc = orc.quant_fp8_rows(x.cpu().numpy(), block=32, rule=0)
     assert (codes.cpu().numpy() == oc).all() and (scales.cpu().numpy() == osc).all()
     assert rel_err(y.cpu().numpy(), orc.gemv_fp8(W.cpu().numpy(), s.cpu().numpy(), v.cpu().numpy())) <= 1e-4
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_prefill_in_a_graph(m, fmt):
+    """moe_expert_prefill captured in a graph: the call's tile counters and
+    tile list are rebuilt by its own first launch on every replay, so each
+    replay equals the eager result bit for bit."""
+    if fmt == "nvfp4":
+        wl = sg.Workload("pf_graph", 95, 2560, 640, 64, 10, "nvfp4", 1, 300, False, "zipf", 1.1, 0x18, 0x48, False)
+    else:
+        wl = sg.Workload("pf_graph_mx", 96, 4096, 2880, 48, 6, "mxfp4", 1, 60, False, "zipf", 1.1, 121, 129, True)
+    T = wl.T
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    blocks = layer_blocks(wl, 0)
+    ptrs = m.expert_ptr_table(blocks)
+    x = sg.activations(wl, 0, 0, T=T, device="cuda")
+    idx, w = sg.routing(wl, T=T)
+    idx, w = idx.cuda(), w.cuda()
+    ws = m.alloc_workspace(d, T, m.MOE_MODE_PREFILL)
+    od = m.MOE_OUT_BF16 if wl.out_bf16 else m.MOE_OUT_F32
+    out = torch.empty((T, wl.H), dtype=torch.bfloat16 if wl.out_bf16 else torch.float32, device="cuda")
+    view = torch.int16 if wl.out_bf16 else torch.int32
+
+    def run():
+        m.moe_expert_prefill(d, x, T, ptrs, idx, w, out, od, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    assert torch.isfinite(ref.float()).all()
+    g = capture(run)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)  # the workspace carries nothing from one call to the next
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(view), ref.view(view)), rep
+        eager_noise()

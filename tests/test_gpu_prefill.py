@@ -376,6 +376,26 @@ def test_prefill_deterministic(m):
         assert torch.equal(again.view(torch.int32), first.view(torch.int32))
 
 
+def test_prefill_workspace_reused_across_routings(m):
+    """Two calls with different routings on one workspace (and a third
+    repeating the first): each equals the same call on a fresh workspace bit
+    for bit, so no counter, tile list or cached activation carries over."""
+    wl = wl_small("nvfp4", 2560, 640, 48, 10, 200)
+    blocks = layer_blocks(wl, 0)
+    x = sg.activations(wl, 0, 0, T=200, device="cuda")
+    routes = [sg.routing(wl, T=200, layer=0), sg.routing(wl, T=200, layer=1, zipf_s=0.0)]
+    fresh = [run_gpu(m, wl, blocks, x, i.cuda(), w.cuda(), False, dbg=False)["out_raw"].clone() for i, w in routes]
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    ws = m.alloc_workspace(d, 200, m.MOE_MODE_PREFILL)
+    ptrs = m.expert_ptr_table(blocks)
+    out = torch.empty((200, wl.H), dtype=torch.float32, device="cuda")
+    for r in (0, 1, 0):
+        i, w = routes[r]
+        m.moe_expert_prefill(d, x, 200, ptrs, i.cuda(), w.cuda(), out, m.MOE_OUT_F32, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), fresh[r].view(torch.int32)), r
+
+
 def test_prefill_invalid_expert_index_gives_nan_row(m):
     wl = wl_small("nvfp4", 512, 128, 8, 2, 5)
     blocks = layer_blocks(wl, 0)
