@@ -44,7 +44,8 @@ class moe_shared(C.Structure):
 
 class moe_prefill_debug(C.Structure):
     _fields_ = [("x_bf16", C.c_void_p), ("x_codes", C.c_void_p), ("x_scales", C.c_void_p), ("h_pre", C.c_void_p),
-                ("h_q", C.c_void_p), ("perm", C.c_void_p), ("off", C.c_void_p)]
+                ("h_q", C.c_void_p), ("perm", C.c_void_p), ("off", C.c_void_p),
+                ("tile_wait_polls", C.c_int32), ("tile_wait_unmet", C.c_int32)]
 
 
 class moe_tier_stats(C.Structure):
@@ -172,7 +173,7 @@ def moe_expert_prefill(d, x, T, expert_ptrs, idx, w, out, out_dtype, ws, ws_byte
     """dbg: None or a dict with any of the moe_prefill_debug member names -> tensors."""
     db = None
     if dbg is not None:
-        db = C.byref(moe_prefill_debug(**{k: _ptr(v) for k, v in dbg.items()}))
+        db = C.byref(moe_prefill_debug(**{k: (v if isinstance(v, int) else _ptr(v)) for k, v in dbg.items()}))
     wsb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check(lib.moe_expert_prefill(C.byref(d), _ptr(x), T, _ptr(expert_ptrs), _ptr(idx), _ptr(w), _ptr(out),
                                   out_dtype, _ptr(ws), wsb, db, _stream(stream)))

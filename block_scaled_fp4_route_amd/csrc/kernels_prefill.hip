@@ -932,6 +932,7 @@ __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, con
 
 // Bound of the down part's wait for its tile's h~, in polls of ~256 cycles
 // (~0.4 s): a wait that ends unmet poisons the tile's outputs with NaN.
+// (The debug controls can lower the bound and make every wait unmet.)
 constexpr int kTileWaitPolls = 1 << 22;
 
 // The down part of workgroup bid of the GEMM launch (lds: 2 * kBM_NV2 *
@@ -939,7 +940,7 @@ constexpr int kTileWaitPolls = 1 << 22;
 // done[4 * tile] reaches `need`, the count of the tile's gate/up workgroups.
 template <bool SL>
 __device__ __forceinline__ void down_part(const GemmArgs& a, __bf16* lds, uint8_t* sl, int bid, const int* done,
-                                          int need) {
+                                          int need, int max_polls) {
     int tile, nt;
     if (!map_tile_b(bid, a.ntiles[0], a.NT, tile, nt)) return;
     const int e = a.tile_e[tile], m0 = a.tile_m[tile];
@@ -952,7 +953,7 @@ __device__ __forceinline__ void down_part(const GemmArgs& a, __bf16* lds, uint8_
     if (threadIdx.x == 0) {
         int c = 0, polls = 0;
         while ((c = __hip_atomic_load(done + 4 * tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need &&
-               ++polls < kTileWaitPolls)
+               ++polls < max_polls)
             __builtin_amdgcn_s_sleep(4);
         *flag = c >= need;
     }
@@ -1011,6 +1012,8 @@ struct GemmPair {
     GemmArgs gu, dn;
     int ngu;
     int* done;
+    int need;       // publications a down tile waits for (NT of gate/up; more: a control)
+    int max_polls;  // bound of each wait
 };
 template <bool SL>
 __global__ __launch_bounds__(256, 2) void k_gemms_nv(GemmPair f) {
@@ -1025,7 +1028,8 @@ __global__ __launch_bounds__(256, 2) void k_gemms_nv(GemmPair f) {
         __syncthreads();
         if (threadIdx.x == 0) __hip_atomic_fetch_add(f.done + 4 * tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        down_part<SL>(f.dn, lds, reinterpret_cast<uint8_t*>(lds + 2 * kBM_NV2 * kBKDown), b - f.ngu, f.done, f.gu.NT);
+        down_part<SL>(f.dn, lds, reinterpret_cast<uint8_t*>(lds + 2 * kBM_NV2 * kBKDown), b - f.ngu, f.done, f.need,
+                      f.max_polls);
     }
 }
 
@@ -1427,6 +1431,8 @@ hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const floa
         gd.a_bytes = (uint32_t)((size_t)n * I * 2);
         GemmPair gp;
         gp.gu = ga; gp.dn = gd; gp.ngu = (int)gemm_grid(mt, ga.NT); gp.done = reinterpret_cast<int*>(L.rec);
+        gp.need = ga.NT + (dbg && dbg->tile_wait_unmet ? 1 : 0);
+        gp.max_polls = dbg && dbg->tile_wait_polls > 0 ? dbg->tile_wait_polls : kTileWaitPolls;
         const dim3 grid((unsigned)gp.ngu + gemm_grid(mt, gd.NT));
         if (I <= kDownSclMaxI)
             hipLaunchKernelGGL(k_gemms_nv<true>, grid, dim3(256), 0, s, gp);

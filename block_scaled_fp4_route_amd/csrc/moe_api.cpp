@@ -260,6 +260,8 @@ int moe_expert_prefill(const moe_desc* d, const float* x, int32_t T, const void*
         pd.h_q = dbg->h_q;
         pd.perm = dbg->perm;
         pd.off = dbg->off;
+        pd.tile_wait_polls = dbg->tile_wait_polls;
+        pd.tile_wait_unmet = dbg->tile_wait_unmet;
     }
     return hip_status(moe::launch_prefill(d->format, d->H, d->I, d->E, d->k, T, x, expert_ptrs, idx, w, out,
                                           out_dtype == MOE_OUT_BF16, ws, dbg ? &pd : nullptr,

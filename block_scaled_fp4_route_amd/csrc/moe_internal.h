@@ -63,6 +63,8 @@ struct PrefillDebug {
     float* h_q;
     int32_t* perm;
     int32_t* off;
+    int tile_wait_polls;  // > 0: poll limit of the GEMM launch's waits
+    int tile_wait_unmet;  // nonzero: those waits ask for one more publication than exists
 };
 hipError_t launch_prefill(int fmt, int H, int I, int E, int k, int T, const float* x,
                           const void* const* expert_ptrs, const int32_t* idx, const float* w, void* out,

@@ -92,6 +92,11 @@ typedef struct moe_prefill_debug {
     float *h_q;         /* [T*k][I] h~ (the rounded h, as fp32), grouped order */
     int32_t *perm;      /* [T*k] assignment id t*k+j at each grouped position */
     int32_t *off;       /* [E+1] first grouped position of each expert; off[E] = T*k */
+    /* Controls of the NVFP4 GEMM launch's bounded wait (down tiles wait for
+     * their gate/up tiles; a wait that ends unmet writes NaN over the tile's
+     * outputs). 0 and 0: the library's behaviour. */
+    int32_t tile_wait_polls;  /* > 0: poll limit instead of the library's (about 0.4 s) */
+    int32_t tile_wait_unmet;  /* nonzero: every wait asks for one more gate/up tile than exists */
 } moe_prefill_debug;
 
 /* ---------------------------------------------------------------------- */

@@ -396,6 +396,32 @@ def test_prefill_workspace_reused_across_routings(m):
         assert torch.equal(out.view(torch.int32), fresh[r].view(torch.int32)), r
 
 
+def test_prefill_unmet_tile_wait_poisons_outputs(m):
+    """The NVFP4 GEMM launch's down tiles wait (bounded) for their gate/up
+    tiles; a wait that ends unmet writes NaN over the tile's outputs instead
+    of using an incomplete h~. Forced from the host: every wait asks for one
+    more publication than exists, with a short poll limit. The call ends,
+    every output is NaN, and the next ordinary call on the same workspace is
+    bit-identical to a fresh one."""
+    wl = wl_small("nvfp4", 512, 128, 8, 2, 40)
+    blocks = layer_blocks(wl, 0)
+    x = sg.activations(wl, 0, 0, T=40, device="cuda")
+    idx, w = sg.routing(wl, T=40)
+    idx, w = idx.cuda(), w.cuda()
+    ref = run_gpu(m, wl, blocks, x, idx, w, False, dbg=False)["out_raw"].clone()
+    d = m.desc(wl.H, wl.I, wl.E, wl.k, wl.fmt)
+    ws = m.alloc_workspace(d, 40, m.MOE_MODE_PREFILL)
+    ptrs = m.expert_ptr_table(blocks)
+    out = torch.empty((40, wl.H), dtype=torch.float32, device="cuda")
+    m.moe_expert_prefill(d, x, 40, ptrs, idx, w, out, m.MOE_OUT_F32, ws,
+                         dbg={"tile_wait_polls": 16, "tile_wait_unmet": 1})
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    m.moe_expert_prefill(d, x, 40, ptrs, idx, w, out, m.MOE_OUT_F32, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
 def test_prefill_invalid_expert_index_gives_nan_row(m):
     wl = wl_small("nvfp4", 512, 128, 8, 2, 5)
     blocks = layer_blocks(wl, 0)
