@@ -42,13 +42,13 @@ METRIC = "MoE layer tokens/s and achieved HBM GB/s (decode), MFMA TFLOP/s (prefi
 # *_prefill: every kernel of one moe_expert_prefill call.
 # fp8_act_quant / fp8_gemv: the one kernel of each call.
 TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
-    "qwen_decode": (38256128, "59e88a0decc5560a"),
-    "qwen_layer_decode": (28344013, "59e88a0decc5560a"),
-    "deepseek_decode": (114379776, "59e88a0decc5560a"),
-    "qwen_prefill": (2692465664, "0dd5e43931fef604"),
-    "deepseek_prefill": (7298339226, "0dd5e43931fef604"),
-    "fp8_act_quant": (21128192, "3e24836c4e0819a4"),
-    "fp8_gemv": (21209088, "3e24836c4e0819a4"),
+    "qwen_decode": (38256128, "4036827fbed01d9d"),
+    "qwen_layer_decode": (28344013, "4036827fbed01d9d"),
+    "deepseek_decode": (114368512, "4036827fbed01d9d"),
+    "qwen_prefill": (2692449178, "09cb38ed9374f9a1"),
+    "deepseek_prefill": (7298305536, "09cb38ed9374f9a1"),
+    "fp8_act_quant": (21128192, "4d7a263804fc10fd"),
+    "fp8_gemv": (21209088, "4d7a263804fc10fd"),
 }
 TRAFFIC_SOURCES = {  # kernel sources behind each workload's figure
     "decode": ["kernels_decode.hip", "moe_device.h", "moe_internal.h"],
