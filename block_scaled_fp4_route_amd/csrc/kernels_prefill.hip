@@ -993,8 +993,9 @@ __device__ __forceinline__ void down_part(const GemmArgs& a, __bf16* lds, uint8_
         down_nv_tile<8, kBM_NV2, SL>(a, lds, sl, e, base, rows, nt);
 }
 
+// ---------------------------------------------------------------------------
 // 4c. The two NVFP4 GEMMs in one launch. Workgroups 0 .. ngu-1 run gate/up
-// (k_gateup's tiles), workgroups ngu .. the down GEMM of the same tiles; ngu
+// (gateup_part), workgroups ngu .. the down GEMM of the same tiles; ngu
 // is a multiple of 8. Down workgroup (tile t, N-tile) starts only once the
 // NT gate/up workgroups of tile t have published its h~ rows: each of those
 // waits until its own stores have reached L2, then adds 1 to done[4t] (an
