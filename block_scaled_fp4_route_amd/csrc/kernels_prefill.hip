@@ -674,7 +674,7 @@ template <int BK, int RB, int MR, bool SL, bool F16, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
                                          uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
-                                         __bf16* lds, const uint8_t* slds, int srow0) {
+                                         __bf16* lds, const uint8_t* slds, const int (&srow)[4]) {
     constexpr int SPR = BK / 8;       // 16-byte pieces per A row
     constexpr int NAI = MR * SPR / 256;  // A loads per wave per chunk (MR rows x SPR pieces over 256 lanes)
     static_assert(NAI >= 1 && NAI * 256 == MR * SPR && RB * 16 <= MR, "A tile shape");
@@ -747,7 +747,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
 #pragma unroll
             for (int i = 0; i < NB; i++) bc[cb][i] = bw[cb][i];
             if constexpr (SL) {
-                const uint8_t* sp = slds + (brow[cb] - srow0) * (KTOT / 16) + ch * (BK / 16) + (QK / 16) * g;
+                const uint8_t* sp = slds + srow[cb] * (KTOT / 16) + ch * (BK / 16) + (QK / 16) * g;
                 sc[cb] = NB == 1 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : *reinterpret_cast<const uint32_t*>(sp);
             } else {
                 sc[cb] = bs[cb];
@@ -805,11 +805,21 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
 
 constexpr int kBKGate = 256;  // K chunk of the gate/up GEMM (K = H)
 constexpr int kBKDown = 128;  // K chunk of the down GEMM (K = I)
+constexpr int kDownSclMaxI = 1024;  // I up to which the down GEMM stages its scales (see 4b)
+// staged gate/up scale bytes that fit after 32 KB of A tiles in the GEMM
+// launch's LDS (2 * kBM_NV2 * kBKDown bf16 + 256 * kDownSclMaxI / 16 bytes)
+constexpr int kGateSclMax = 2 * kBM_NV2 * kBKDown * 2 + 256 * kDownSclMaxI / 16 - 32768;
 
 // One gate/up tile: RB row blocks of the tile's rows, K chunks of BK, the A
 // tile staged as MR rows.
-template <int RB, int BK, int MR>
+// SL: the scales of the workgroup's 256 weight rows (gate columns n0 .. +128
+// then the matching up columns, H/16 bytes each, two contiguous ranges of
+// the block) are staged in LDS at lds + 32 KB first (tiles of up to 32 rows,
+// whose A tiles take the first 32 KB; 16 H bytes), so the K loop loads only
+// codes from memory.
+template <int RB, int BK, int MR, bool SL>
 __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, int e, int base, int rows, int nt) {
+    static_assert(!SL || 2 * MR * BK * 2 <= 32768, "staged scales follow the A tiles");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int c0 = nt * 128 + 32 * wave;
@@ -818,6 +828,21 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
     const uint32_t scl_off = (uint32_t)3 * I * H / 2;         // gate scales then up scales, H/16 each
     const int m16 = lane & 15;
     const int brow[4] = {c0 + m16, c0 + 16 + m16, I + c0 + m16, I + c0 + 16 + m16};
+    // slice row of each column block's scales: gate rows 0..127, up rows 128..255
+    const int cl = 32 * wave + m16;
+    const int srow[4] = {cl, cl + 16, 128 + cl, 128 + cl + 16};
+    uint8_t* sl = reinterpret_cast<uint8_t*>(lds) + 32768;
+    if constexpr (SL) {
+        // 1 KB loads, older than the K loop's first loads (its first wait
+        // covers them)
+        const uint32_t SB = (uint32_t)H / 16, half = 128 * SB;
+        const uint32_t g0 = scl_off + (uint32_t)(nt * 128) * SB, u0 = scl_off + (uint32_t)(I + nt * 128) * SB;
+        const rsrc_t rw = make_rsrc(blk, a.block_bytes);
+        for (uint32_t ii = wave; ii * 1024 < 2 * half; ii += 4) {
+            const uint32_t b = ii * 1024 + 16 * lane;
+            load_lds16(rw, sl + ii * 1024, b < half ? g0 + b : (b < 2 * half ? u0 + (b - half) : kOOB));
+        }
+    }
     const __bf16* X = reinterpret_cast<const __bf16*>(a.a_src);
     const int* perm = a.perm;
     const int k = a.k;
@@ -827,8 +852,8 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
     for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<BK, RB, MR, false, true>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H,
-                                      lds, nullptr, 0);
+    nv_kloop<BK, RB, MR, SL, true>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H,
+                                   lds, sl, srow);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i;
     // the sums carry the row's 2^t of the fp16 x~ (exact to undo)
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
@@ -876,16 +901,26 @@ __device__ __forceinline__ int gateup_part(const GemmArgs& a, __bf16* lds, int b
     const int base = a.off[e] + m0;
     // the K loop is specialised on the tile's row blocks (wave-uniform); a
     // 128-row tile takes 128-wide K chunks so that its A tile fits the same LDS
-    if (rows <= 16)
-        gateup_nv_tile<1, kBKGate, 16>(a, lds, e, base, rows, nt);
-    else if (rows <= 32)
-        gateup_nv_tile<2, kBKGate, 32>(a, lds, e, base, rows, nt);
-    else if (rows <= 48)
-        gateup_nv_tile<3, kBKGate, 48>(a, lds, e, base, rows, nt);
-    else if (rows <= 64)
-        gateup_nv_tile<4, kBKGate, 64>(a, lds, e, base, rows, nt);
-    else
-        gateup_nv_tile<8, 128, kBM_NV2>(a, lds, e, base, rows, nt);
+    // tiles of up to 32 rows stage their scales where the LDS holds them
+    // (16 H bytes after the 32 KB of A tiles, within the launch's 80 KB)
+    const bool sl_fits = 16 * a.H <= kGateSclMax;
+    if (rows <= 16) {
+        if (sl_fits)
+            gateup_nv_tile<1, kBKGate, 16, true>(a, lds, e, base, rows, nt);
+        else
+            gateup_nv_tile<1, kBKGate, 16, false>(a, lds, e, base, rows, nt);
+    } else if (rows <= 32) {
+        if (sl_fits)
+            gateup_nv_tile<2, kBKGate, 32, true>(a, lds, e, base, rows, nt);
+        else
+            gateup_nv_tile<2, kBKGate, 32, false>(a, lds, e, base, rows, nt);
+    } else if (rows <= 48) {
+        gateup_nv_tile<3, kBKGate, 48, false>(a, lds, e, base, rows, nt);
+    } else if (rows <= 64) {
+        gateup_nv_tile<4, kBKGate, 64, false>(a, lds, e, base, rows, nt);
+    } else {
+        gateup_nv_tile<8, 128, kBM_NV2, false>(a, lds, e, base, rows, nt);
+    }
     return tile;
 }
 
@@ -895,7 +930,6 @@ __device__ __forceinline__ int gateup_part(const GemmArgs& a, __bf16* lds, int b
 // SL (I <= kDownSclMaxI): the scales of the 256 weight rows (I/16 bytes each,
 // contiguous in the block) are staged in LDS first; the K loop then reads
 // only codes from memory.
-constexpr int kDownSclMaxI = 1024;
 
 template <int RB, int MR, bool SL>
 __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, const uint8_t* sl, int e, int base,
@@ -908,6 +942,7 @@ __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, con
     const uint32_t scl_off = (uint32_t)3 * I * H / 2 + (uint32_t)2 * I * H / 16;  // down scales [H][I/16]
     const int m16 = lane & 15;
     const int brow[4] = {n0 + m16, n0 + 16 + m16, n0 + 32 + m16, n0 + 48 + m16};
+    const int srow[4] = {brow[0] - nt * 256, brow[1] - nt * 256, brow[2] - nt * 256, brow[3] - nt * 256};
     const __bf16* Hq = reinterpret_cast<const __bf16*>(a.a_src);
     auto a_row = [&](int r) { return (base + r) * I; };  // 0 <= r < rows
     f32x4 acc[RB][4];
@@ -916,7 +951,7 @@ __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, con
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     nv_kloop<kBKDown, RB, MR, SL, false>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds,
-                                  sl, nt * 256);
+                                  sl, srow);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
 #pragma unroll
