@@ -170,7 +170,8 @@ def moe_layer_decode_noalloc(d, x, Wr, expert_ptrs, shared, y, idx_out, w_out, s
 
 
 def moe_expert_prefill(d, x, T, expert_ptrs, idx, w, out, out_dtype, ws, ws_bytes=None, dbg=None, stream=None):
-    """dbg: None or a dict with any of the moe_prefill_debug member names -> tensors."""
+    """dbg: None or a dict with any of the moe_prefill_debug member names -> tensors
+    (the two wait controls take ints)."""
     db = None
     if dbg is not None:
         db = C.byref(moe_prefill_debug(**{k: (v if isinstance(v, int) else _ptr(v)) for k, v in dbg.items()}))

@@ -84,6 +84,33 @@ def test_decode_argument_errors():
         == m.MOE_ERR_UNSUPPORTED
 
 
+def test_prefill_argument_errors():
+    d = m.desc(2560, 640, 512, 10, "nvfp4")
+    need = m.moe_workspace_bytes(d, 100, m.MOE_MODE_PREFILL)
+    f32 = m.MOE_OUT_F32
+
+    def call(d=d, x=FAKE, T=100, ptrs=FAKE, idx=FAKE, w=FAKE, out=FAKE, od=f32, ws=FAKE, wsb=need):
+        return _err(m.moe_expert_prefill, d, x, T, ptrs, idx, w, out, od, ws, wsb, None, 0)
+
+    assert call(T=0) == m.MOE_ERR_ARG
+    assert call(T=-3) == m.MOE_ERR_ARG
+    assert call(x=None) == m.MOE_ERR_ARG
+    assert call(x=ODD) == m.MOE_ERR_ARG          # x: 16-byte alignment
+    assert call(ptrs=None) == m.MOE_ERR_ARG
+    assert call(idx=None) == m.MOE_ERR_ARG
+    assert call(w=None) == m.MOE_ERR_ARG
+    assert call(out=ODD) == m.MOE_ERR_ARG
+    assert call(od=7) == m.MOE_ERR_ARG            # unknown output type
+    assert call(ws=None, wsb=0) == m.MOE_ERR_WORKSPACE
+    assert call(wsb=need - 256) == m.MOE_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == m.MOE_ERR_WORKSPACE   # 256-byte alignment
+    # no kernel for H % 256 != 0 (NVFP4) or H % 512 != 0 (MXFP4), nor for a
+    # token count whose rounded activations exceed 2 GiB
+    assert call(d=m.desc(2560 + 128, 640, 512, 10, "nvfp4"), wsb=1 << 40) == m.MOE_ERR_UNSUPPORTED
+    assert call(d=m.desc(2560 + 256, 640, 384, 6, "mxfp4"), wsb=1 << 40) == m.MOE_ERR_UNSUPPORTED
+    assert call(T=1 << 20, wsb=1 << 40) == m.MOE_ERR_UNSUPPORTED
+
+
 def test_layer_decode_argument_errors():
     d = m.desc(2560, 640, 512, 10, "nvfp4")
     need = m.moe_workspace_bytes(d, 1, m.MOE_MODE_DECODE)
