@@ -337,6 +337,15 @@ def test_prefill_tile_row_counts(m, orc, fmt):
     full_check(m, orc, wl, T, routing=counts_routing(counts, T), tag=f"tile_row_counts_{fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_prefill_largest_expert_count_and_top_k(m, orc, fmt):
+    """E = 1024 experts (the tile list's scans at their full 1024 threads)
+    and top-32 routing (the combine's widest groups), uniform routing so
+    that most experts hold a few rows."""
+    wl = wl_small(fmt, 512, 128 if fmt == "nvfp4" else 64, 1024, 32, 80, s=0.0)
+    full_check(m, orc, wl, 80, tag=f"largest_E_k_{fmt}")
+
+
 def test_prefill_mxfp4_deepseek_shape_small_E(m, orc):
     wl = wl_small("mxfp4", 4096, 2880, 12, 6, 20, s=0.0)
     full_check(m, orc, wl, 20)
