@@ -655,8 +655,8 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t d, float s) {
 // consecutive rows on distinct bank groups. Rows past `rows` take the
 // out-of-range offset (zeros, no memory traffic; their sums are never stored).
 // SL: the block scales of the workgroup's weight rows were staged in LDS
-// before the loop (slds: row n - srow0 at (n - srow0) * KTOT/16, the rows'
-// scale bytes as stored), so the loop loads only codes from memory. A scale
+// before the loop (slds: the scale bytes of column block cb's row, as stored,
+// at srow[cb] * KTOT/16), so the loop loads only codes from memory. A scale
 // load from memory takes a whole cache line for 2-4 bytes of each row; staged,
 // the rows' scales arrive as contiguous lines once.
 
