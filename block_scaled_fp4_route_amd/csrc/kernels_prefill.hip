@@ -670,18 +670,26 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off)
 // code that uses a or b after it cannot be scheduled before it.
 __device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
-template <int BK, int RB, int MR, bool SL, bool F16, class AROW>
+// SR (gate/up tiles of 8 row blocks, 128-wide chunks, one weight set): the
+// scales go through a ring of two 8 KB halves at slds, each holding four
+// chunks' scale bytes of the workgroup's 256 weight rows (slice row r: 32
+// bytes at r*32; gate rows sr_g0.., up rows sr_u0.., srow as for SL),
+// staged one group of four chunks ahead with 1 KB loads of 32 contiguous
+// bytes per row.
+template <int BK, int RB, int MR, bool SL, bool F16, bool SR, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
                                          uint32_t codes_off, uint32_t scl_off, const int (&brow)[4], int KTOT,
-                                         __bf16* lds, const uint8_t* slds, const int (&srow)[4]) {
+                                         __bf16* lds, const uint8_t* slds, const int (&srow)[4], int sr_g0 = 0,
+                                         int sr_u0 = 0) {
     constexpr int SPR = BK / 8;       // 16-byte pieces per A row
     constexpr int NAI = MR * SPR / 256;  // A loads per wave per chunk (MR rows x SPR pieces over 256 lanes)
     static_assert(NAI >= 1 && NAI * 256 == MR * SPR && RB * 16 <= MR, "A tile shape");
     constexpr int QK = BK / 4;        // K per lane group
     constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
     constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
-    constexpr int NBL = SL ? 4 * NB : 4 * (NB + 1);  // weight loads per lane per chunk (codes [+ scales])
+    constexpr int NBL = SL || SR ? 4 * NB : 4 * (NB + 1);  // weight loads per lane per chunk (codes [+ scales])
+    static_assert(!SR || (!SL && NB == 1 && RB >= 8), "scale ring: 8 row blocks, 128-wide chunks");
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, m16 = lane & 15;
     const rsrc_t ra = make_rsrc(A, a_bytes);
@@ -719,10 +727,25 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, on ? boff[cb] + ch * (BK / 2) + 16 * i : kOOB, 0, 0);
                 bw[cb][i] = uint4{v[0], v[1], v[2], v[3]};
             }
-            if constexpr (!SL) {
+            if constexpr (!SL && !SR) {
                 const uint32_t so = on ? soff[cb] + ch * (BK / 16) : kOOB;
                 bs[cb] = NB == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0)
                                  : __builtin_amdgcn_raw_buffer_load_b32(rb, so, 0, 0);
+            }
+        }
+    };
+    // scale ring (SR): group G = chunks 4G .. 4G+3 -> half G & 1; two 1 KB
+    // loads per wave (slice rows (2 wave + i) * 32 .. +31, 32 bytes each)
+    uint8_t* const srb = const_cast<uint8_t*>(slds);
+    auto stage = [&](int G) {
+        if constexpr (SR) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int P = (wave * 2 + i) * 64 + lane, r = P >> 1, q = P & 1;
+                const uint32_t row = r < 128 ? (uint32_t)(sr_g0 + r) : (uint32_t)(sr_u0 + r - 128);
+                const uint32_t b = 32u * G + 16u * q;
+                load_lds16(rb, srb + (G & 1) * 8192 + (wave * 2 + i) * 1024,
+                           b < (uint32_t)(KTOT / 16) ? scl_off + row * (KTOT / 16) + b : kOOB);
             }
         }
     };
@@ -731,6 +754,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
     constexpr int NSET = RB >= 8 ? 1 : 2;
     uint4 b0[4][NB], b1[4][NB];
     uint32_t s0[4], s1[4];
+    stage(0);  // older than A(0): the first wait covers it
     issue_a(0, 0);
     load_b(0, b0, s0);
     if constexpr (NSET > 1) load_b(1, b1, s1);
@@ -739,14 +763,18 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
     // chunk ch+NSET, load A(ch+1) into the other LDS buffer, compute, then wait
     // for A(ch+1): the barrier also ends every wave's reads of this chunk's
     // buffer, which A(ch+2) overwrites
-    auto step = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4]) {
+    auto step = [&](int ch, uint4 (&bw)[4][NB], uint32_t (&bs)[4], auto stg) {
+        constexpr bool STG = decltype(stg)::value;  // this step stages the next scale group
         uint4 bc[4][NB];
         uint32_t sc[4];
 #pragma unroll
         for (int cb = 0; cb < 4; cb++) {
 #pragma unroll
             for (int i = 0; i < NB; i++) bc[cb][i] = bw[cb][i];
-            if constexpr (SL) {
+            if constexpr (SR) {
+                const uint8_t* sp = srb + ((ch >> 2) & 1) * 8192 + srow[cb] * 32 + (ch & 3) * (BK / 16) + (QK / 16) * g;
+                sc[cb] = (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
+            } else if constexpr (SL) {
                 const uint8_t* sp = slds + srow[cb] * (KTOT / 16) + ch * (BK / 16) + (QK / 16) * g;
                 sc[cb] = NB == 1 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : *reinterpret_cast<const uint32_t*>(sp);
             } else {
@@ -754,6 +782,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
             }
         }
         issue_a(ch + 1, (ch + 1) & 1);
+        if constexpr (STG) stage((ch >> 2) + 1);  // into the half group (ch/4) - 1 used
         load_b(ch + NSET, bw, bs);
         if (ch < nchunks) {
             const __bf16* At = lds + (size_t)(ch & 1) * MR * BK;
@@ -791,15 +820,25 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
                 }
             }
         }
-        vm_wait_barrier<NBL>();
+        // A(ch+1) landed (younger: the staged scales, if any, and B(ch+NSET))
+        vm_wait_barrier<STG ? NBL + 2 : NBL>();
     };
+    using Y = std::integral_constant<bool, true>;
+    using N = std::integral_constant<bool, false>;
     if constexpr (NSET > 1) {
         for (int ch = 0; ch < nchunks; ch += 2) {
-            step(ch, b0, s0);
-            step(ch + 1, b1, s1);
+            step(ch, b0, s0, N{});
+            step(ch + 1, b1, s1, N{});
+        }
+    } else if constexpr (SR) {
+        for (int ch = 0; ch < nchunks; ch += 4) {
+            step(ch, b0, s0, Y{});
+            step(ch + 1, b0, s0, N{});
+            step(ch + 2, b0, s0, N{});
+            step(ch + 3, b0, s0, N{});
         }
     } else {
-        for (int ch = 0; ch < nchunks; ch++) step(ch, b0, s0);
+        for (int ch = 0; ch < nchunks; ch++) step(ch, b0, s0, N{});
     }
 }
 
@@ -852,8 +891,12 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
     for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<BK, RB, MR, SL, true>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H,
-                                   lds, sl, srow);
+    // 8 row blocks (128-wide chunks, whose A tiles take 64 KB): the scales go
+    // through a 16 KB ring after the A tiles
+    constexpr bool SR = RB >= 8;
+    nv_kloop<BK, RB, MR, SL, true, SR>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H,
+                                       lds, SR ? reinterpret_cast<uint8_t*>(lds) + 65536 : sl, srow, nt * 128,
+                                       I + nt * 128);
     // epilogue: lane holds column c0 + 16 cbg + m16, rows 16 rb + 4 g + i;
     // the sums carry the row's 2^t of the fp16 x~ (exact to undo)
     __bf16* hq = reinterpret_cast<__bf16*>(a.out);
@@ -950,7 +993,7 @@ __device__ __forceinline__ void down_nv_tile(const GemmArgs& a, __bf16* lds, con
     for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    nv_kloop<kBKDown, RB, MR, SL, false>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds,
+    nv_kloop<kBKDown, RB, MR, SL, false, false>(acc, Hq, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, I, lds,
                                   sl, srow);
     float* Y = reinterpret_cast<float*>(a.out);
     const int g = lane >> 4;
