@@ -45,8 +45,8 @@ TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
     "qwen_decode": (38256128, "4036827fbed01d9d"),
     "qwen_layer_decode": (28344013, "4036827fbed01d9d"),
     "deepseek_decode": (114368512, "4036827fbed01d9d"),
-    "qwen_prefill": (2628584038, "7391a3f116e9f2e3"),
-    "deepseek_prefill": (7298183782, "7391a3f116e9f2e3"),
+    "qwen_prefill": (2568133939, "5a953b2bd06479da"),
+    "deepseek_prefill": (7298452787, "5a953b2bd06479da"),
     "fp8_act_quant": (21128192, "4d7a263804fc10fd"),
     "fp8_gemv": (21209088, "4d7a263804fc10fd"),
 }
