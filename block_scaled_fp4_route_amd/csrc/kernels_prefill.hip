@@ -670,12 +670,12 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint8_t* lds, uint32_t off)
 // code that uses a or b after it cannot be scheduled before it.
 __device__ __forceinline__ void order_point(int& a, int& b) { asm volatile("" : "+v"(a), "+v"(b)::"memory"); }
 
-// SR (gate/up tiles of 8 row blocks, 128-wide chunks, one weight set): the
-// scales go through a ring of two 8 KB halves at slds, each holding four
-// chunks' scale bytes of the workgroup's 256 weight rows (slice row r: 32
-// bytes at r*32; gate rows sr_g0.., up rows sr_u0.., srow as for SL),
-// staged one group of four chunks ahead with 1 KB loads of 32 contiguous
-// bytes per row.
+// SR (gate/up tiles that do not stage all their scales): the scales go
+// through a ring of two 8 KB halves at slds, each holding one group of
+// chunks' scale bytes of the workgroup's 256 weight rows (4 chunks of 128 or
+// 2 of 256: slice row r's 32 bytes at r*32; gate rows sr_g0.., up rows
+// sr_u0.., srow as for SL), staged one group ahead with 1 KB loads of 32
+// contiguous bytes per row.
 template <int BK, int RB, int MR, bool SL, bool F16, bool SR, class AROW>
 __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __restrict__ A, uint32_t a_bytes,
                                          AROW a_row, int rows, const void* blk, uint32_t block_bytes,
@@ -689,7 +689,8 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
     constexpr int NB = QK / 32;       // 16-byte code loads per column block (1 or 2)
     constexpr int NS = QK / 8;        // MFMA steps per chunk (4 or 8)
     constexpr int NBL = SL || SR ? 4 * NB : 4 * (NB + 1);  // weight loads per lane per chunk (codes [+ scales])
-    static_assert(!SR || (!SL && NB == 1 && RB >= 8), "scale ring: 8 row blocks, 128-wide chunks");
+    constexpr int GS = 4 / NB;  // chunks per scale group (32 bytes per row)
+    static_assert(!SR || (!SL && (NB == 1 ? RB >= 8 : RB < 8)), "scale ring: one weight set per 128-wide chunk group, two per 256-wide");
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, m16 = lane & 15;
     const rsrc_t ra = make_rsrc(A, a_bytes);
@@ -734,8 +735,8 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
             }
         }
     };
-    // scale ring (SR): group G = chunks 4G .. 4G+3 -> half G & 1; two 1 KB
-    // loads per wave (slice rows (2 wave + i) * 32 .. +31, 32 bytes each)
+    // scale ring (SR): group G = chunks GS*G .. GS*G+GS-1 -> half G & 1; two
+    // 1 KB loads per wave (slice rows (2 wave + i) * 32 .. +31, 32 bytes each)
     uint8_t* const srb = const_cast<uint8_t*>(slds);
     auto stage = [&](int G) {
         if constexpr (SR) {
@@ -772,8 +773,8 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
 #pragma unroll
             for (int i = 0; i < NB; i++) bc[cb][i] = bw[cb][i];
             if constexpr (SR) {
-                const uint8_t* sp = srb + ((ch >> 2) & 1) * 8192 + srow[cb] * 32 + (ch & 3) * (BK / 16) + (QK / 16) * g;
-                sc[cb] = (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
+                const uint8_t* sp = srb + ((ch / GS) & 1) * 8192 + srow[cb] * 32 + (ch % GS) * (BK / 16) + (QK / 16) * g;
+                sc[cb] = NB == 1 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : *reinterpret_cast<const uint32_t*>(sp);
             } else if constexpr (SL) {
                 const uint8_t* sp = slds + srow[cb] * (KTOT / 16) + ch * (BK / 16) + (QK / 16) * g;
                 sc[cb] = NB == 1 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : *reinterpret_cast<const uint32_t*>(sp);
@@ -782,7 +783,7 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
             }
         }
         issue_a(ch + 1, (ch + 1) & 1);
-        if constexpr (STG) stage((ch >> 2) + 1);  // into the half group (ch/4) - 1 used
+        if constexpr (STG) stage(ch / GS + 1);  // into the half group ch/GS - 1 used
         load_b(ch + NSET, bw, bs);
         if (ch < nchunks) {
             const __bf16* At = lds + (size_t)(ch & 1) * MR * BK;
@@ -825,7 +826,12 @@ __device__ __forceinline__ void nv_kloop(f32x4 (&acc)[RB][4], const __bf16* __re
     };
     using Y = std::integral_constant<bool, true>;
     using N = std::integral_constant<bool, false>;
-    if constexpr (NSET > 1) {
+    if constexpr (NSET > 1 && SR) {
+        for (int ch = 0; ch < nchunks; ch += 2) {
+            step(ch, b0, s0, Y{});
+            step(ch + 1, b1, s1, N{});
+        }
+    } else if constexpr (NSET > 1) {
         for (int ch = 0; ch < nchunks; ch += 2) {
             step(ch, b0, s0, N{});
             step(ch + 1, b1, s1, N{});
@@ -891,9 +897,9 @@ __device__ __forceinline__ void gateup_nv_tile(const GemmArgs& a, __bf16* lds, i
     for (int i = 0; i < RB; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // 8 row blocks (128-wide chunks, whose A tiles take 64 KB): the scales go
-    // through a 16 KB ring after the A tiles
-    constexpr bool SR = RB >= 8;
+    // without staged scales (A tiles of up to 64 KB): the scales go through a
+    // 16 KB ring after 64 KB
+    constexpr bool SR = !SL;
     nv_kloop<BK, RB, MR, SL, true, SR>(acc, X, a.a_bytes, a_row, rows, blk, a.block_bytes, codes_off, scl_off, brow, H,
                                        lds, SR ? reinterpret_cast<uint8_t*>(lds) + 65536 : sl, srow, nt * 128,
                                        I + nt * 128);
