@@ -222,7 +222,9 @@ __device__ __forceinline__ void group_block(const int32_t* __restrict__ idx, int
 // ---------------------------------------------------------------------------
 // 2. tile list: experts ordered by row count (descending; ties by index),
 // each split into M-tiles of BM rows, or of BM2 rows if it has at least
-// BM2min (BM2 = 0: one height). One workgroup of 1024 threads, which counts
+// BM2min (BM2 = 0: one height); the tiles in that order are then placed in
+// the slots so that each XCD runs a contiguous part of the heavy experts'
+// tiles (the slot order below). One workgroup of 1024 threads, which counts
 // the rows of every expert itself (an LDS histogram of idx), so that it
 // depends on nothing but the routing and runs beside the grouping.
 //
@@ -321,8 +323,34 @@ __device__ __forceinline__ void tile_list_block(const int32_t* __restrict__ idx,
     if (tid == 0) start[0] = 0;
     if (tid == kGroupThreads - 1) ntiles[0] = v;
     __syncthreads();
-    // one thread per tile slot: its rank r is the last with start[r] <= slot
-    const int used = start[E];
+    // heavy experts (more than one tile) are the ranks 0 .. R-1, their nh
+    // tiles the first in rank order
+    const int R = __syncthreads_count(tid < E && nt_sorted[tid] >= 2);
+    const int used = start[E], nh = start[R];
+    // slot -> tile index in rank order. The GEMM workgroups of slot s run on
+    // XCD s % 8, and slot 8i + x is XCD x's i-th tile. XCD x takes first a
+    // contiguous run of the heavy tiles (nh/8 of them, one more for the first
+    // nh % 8 XCDs), so that the tiles of one heavy expert share few L2s, then
+    // single tiles dealt in rounds (round j: one to every XCD that still has
+    // room, in XCD order), which keeps their mix of heights even. Every XCD
+    // holds used/8 tiles (one more for the first used % 8), so the slots
+    // below `used` are exactly the tiles.
+    auto order = [&](int sl) {
+        const int x = sl & 7, i = sl >> 3;
+        const int hq = nh >> 3, hr = nh & 7, nq = used >> 3, nr = used & 7;
+        const int hx = hq + (x < hr);
+        if (i < hx) return x * hq + min(x, hr) + i;
+        const int j = i - hx;
+        int q = 0;
+#pragma unroll
+        for (int y = 0; y < 8; y++) {
+            const int sy = nq + (y < nr) - hq - (y < hr);  // single tiles of XCD y
+            q += min(sy, j) + (y < x && sy > j);
+        }
+        return nh + q;
+    };
+    // one thread per tile slot: the rank r of its tile u is the last with
+    // start[r] <= u
     const int slots = rec ? max_slots : used;
     for (int sl = tid; sl < slots; sl += kGroupThreads) {
         if (sl >= used) {
@@ -333,12 +361,13 @@ __device__ __forceinline__ void tile_list_block(const int32_t* __restrict__ idx,
             rec[sl] = t;
             continue;
         }
-        int lo = 0, hi = E - 1;  // start[lo] <= sl < start[hi + 1]
+        const int u = order(sl);
+        int lo = 0, hi = E - 1;  // start[lo] <= u < start[hi + 1]
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (start[mid] <= sl) lo = mid; else hi = mid - 1;
+            if (start[mid] <= u) lo = mid; else hi = mid - 1;
         }
-        const int e = ex_sorted[lo], bm = height(cnt[e]), m = sl - start[lo];
+        const int e = ex_sorted[lo], bm = height(cnt[e]), m = u - start[lo];
         tile_e[sl] = e;
         tile_m[sl] = m * bm;
         if (rec) {
@@ -555,9 +584,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_front(FrontArgs f) {
 // Workgroup -> (M-tile, N-tile). Workgroups are dispatched round-robin over
 // the 8 XCDs (each with its own L2), so workgroup b runs on XCD b % 8. M-tile
 // t goes to XCD t % 8 and all NT N-tiles of an M-tile (the same gathered
-// activation rows) to that XCD, one after the other: the tile list is sorted
-// heaviest expert first, so dealing M-tiles round-robin spreads the full
-// tiles evenly over the XCDs. The grid is 8 * ceil(max_tiles / 8) * NT.
+// activation rows) to that XCD, one after the other; the tile list puts the
+// tiles of a heavy expert in few XCDs' slots and balances the tiles per XCD
+// (tile_list_block). The grid is 8 * ceil(max_tiles / 8) * NT.
 // bid: the workgroup's index within its part of the launch (the down part
 // of the GEMM launch starts at a multiple of 8, so a tile's gate/up and down
 // workgroups share an XCD). Returns false for workgroups beyond the real
