@@ -328,19 +328,24 @@ __device__ __forceinline__ void tile_list_block(const int32_t* __restrict__ idx,
     const int R = __syncthreads_count(tid < E && nt_sorted[tid] >= 2);
     const int used = start[E], nh = start[R];
     // slot -> tile index in rank order. The GEMM workgroups of slot s run on
-    // XCD s % 8, and slot 8i + x is XCD x's i-th tile. XCD x takes first a
-    // contiguous run of the heavy tiles (nh/8 of them, one more for the first
-    // nh % 8 XCDs), so that the tiles of one heavy expert share few L2s, then
-    // single tiles dealt in rounds (round j: one to every XCD that still has
-    // room, in XCD order), which keeps their mix of heights even. Every XCD
-    // holds used/8 tiles (one more for the first used % 8), so the slots
-    // below `used` are exactly the tiles.
+    // XCD s % 8, and slot 8i + x is XCD x's i-th tile. Every XCD holds n =
+    // used/8 tiles (one more for the first used % 8), so the slots below
+    // `used` are exactly the tiles. Of them, XCD x takes a contiguous run of
+    // the heavy tiles (hx = nh/8, one more for the first nh % 8 XCDs), so
+    // that the tiles of one heavy expert share few L2s, spread evenly over
+    // its n positions with a heavy tile first (position i is heavy when
+    // ceil((i+1) hx / n) > ceil(i hx / n)): the heavy tiles are bound by
+    // their MFMAs, the single tiles by their weight loads, and mixed they
+    // overlap. The rest are single tiles dealt in rounds (round j: one to
+    // every XCD that still has room, in XCD order), which keeps their mix of
+    // heights even.
     auto order = [&](int sl) {
         const int x = sl & 7, i = sl >> 3;
         const int hq = nh >> 3, hr = nh & 7, nq = used >> 3, nr = used & 7;
-        const int hx = hq + (x < hr);
-        if (i < hx) return x * hq + min(x, hr) + i;
-        const int j = i - hx;
+        const int hx = hq + (x < hr), n = nq + (x < nr);
+        const int c0 = (i * hx + n - 1) / n, c1 = ((i + 1) * hx + n - 1) / n;
+        if (c1 > c0) return x * hq + min(x, hr) + c0;
+        const int j = i - c0;
         int q = 0;
 #pragma unroll
         for (int y = 0; y < 8; y++) {
