@@ -338,7 +338,8 @@ __device__ __forceinline__ void tile_list_block(const int32_t* __restrict__ idx,
     // their MFMAs, the single tiles by their weight loads, and mixed they
     // overlap. The rest are single tiles dealt in rounds (round j: one to
     // every XCD that still has room, in XCD order), which keeps their mix of
-    // heights even.
+    // heights even across XCDs, taken alternately from the largest and the
+    // smallest left, which keeps it even along each XCD's sequence.
     auto order = [&](int sl) {
         const int x = sl & 7, i = sl >> 3;
         const int hq = nh >> 3, hr = nh & 7, nq = used >> 3, nr = used & 7;
@@ -352,7 +353,10 @@ __device__ __forceinline__ void tile_list_block(const int32_t* __restrict__ idx,
             const int sy = nq + (y < nr) - hq - (y < hr);  // single tiles of XCD y
             q += min(sy, j) + (y < x && sy > j);
         }
-        return nh + q;
+        // blocks of 8 (a round) alternate between the largest and the
+        // smallest single tiles left
+        const int ns = used - nh, f = ((q >> 4) << 3) + (q & 7);
+        return nh + (((q >> 3) & 1) ? ns - 1 - f : f);
     };
     // one thread per tile slot: the rank r of its tile u is the last with
     // start[r] <= u
