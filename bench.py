@@ -45,8 +45,8 @@ TRAFFIC: dict = {  # workload: (HBM bytes per call, sources fingerprint)
     "qwen_decode": (38256128, "4036827fbed01d9d"),
     "qwen_layer_decode": (28344013, "4036827fbed01d9d"),
     "deepseek_decode": (114368512, "4036827fbed01d9d"),
-    "qwen_prefill": (2579488358, "fa2325c817ff2595"),
-    "deepseek_prefill": (7297985229, "fa2325c817ff2595"),
+    "qwen_prefill": (2574034842, "5acc77f42e0b0790"),
+    "deepseek_prefill": (7298760090, "5acc77f42e0b0790"),
     "fp8_act_quant": (21128192, "4d7a263804fc10fd"),
     "fp8_gemv": (21209088, "4d7a263804fc10fd"),
 }
