@@ -338,6 +338,23 @@ def test_prefill_tile_row_counts(m, orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("case,counts", [
+    ("all_multi_tile", [129, 200, 257, 300, 140, 130]),
+    ("two_heavy_tiles", [200, 1, 5, 16, 33, 64, 100, 3, 7, 9]),
+    ("few_single_tiles", [130, 140, 150, 160, 170, 1, 2, 3]),
+])
+def test_prefill_tile_order_edges(m, orc, fmt, case, counts):
+    """The tile slots' order (each XCD: a run of the multi-tile experts'
+    tiles spread among single tiles) where it has edges: no single tiles at
+    all (NVFP4), fewer multi-tile tiles than XCDs, and as many whole rounds of
+    8 tiles as of multi-tile tiles (few single tiles left over). Every tile
+    must be run exactly once."""
+    T = sum(counts) // 2
+    wl = wl_small(fmt, 512, 128 if fmt == "nvfp4" else 64, len(counts), 2, T)
+    full_check(m, orc, wl, T, routing=counts_routing(counts, T), tag=f"tile_order_{case}_{fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_prefill_largest_expert_count_and_top_k(m, orc, fmt):
     """E = 1024 experts (the tile list's scans at their full 1024 threads)
     and top-32 routing (the combine's widest groups), uniform routing so
